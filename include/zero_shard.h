@@ -193,7 +193,8 @@ zero_status zero_pack_bucket(const zero_plan* plan, int64_t b, const void* const
  * so results are bit-reproducible.  Columns of dead parameters and the row gap are not
  * written.  If d_flag is not NULL, the call also ORs 1 into *d_flag when any written
  * value is inf or NaN (the fused overflow check); it never clears the flag.
- *   d_rows      device 16-bit, 16-byte aligned; row_stride >= L_b, multiple of 8
+ *   d_rows      device 16-bit, 16-byte aligned, (Nd-1)*row_stride + L_b elements;
+ *               row_stride >= L_b and a multiple of 8
  *   d_live      device uint8[n_params]
  *   d_g32       device float[shard_numel], 16-byte aligned
  * Errors: ZERO_EINVAL for bad index, pointers, alignment or row_stride. */
@@ -238,6 +239,17 @@ zero_status zero_adam_step(const zero_plan* plan, const float* d_g32, float* d_p
  *   d_param_ptrs  device array of n_params pointers to 16-bit flats (numel_i each) */
 zero_status zero_unpack(const zero_plan* plan, int64_t b, const void* d_gathered, void* const* d_param_ptrs,
                         void* stream);
+
+/* Initialise rank r's fp32 master shard from full flat parameters [LLZ INIT: pad each
+ * parameter, view it as [Nd, -1] and clone row r as p32; FR Implémentation simplifiée: the
+ * padding is zeros]: d_p32[shard_offset_i + j] = src_i[shard_start_i + j] when that index is
+ * below numel_i, else +0; the row gaps are set to +0.  Parameters whose d_src_ptrs[i] is NULL
+ * are left as they were.
+ *   d_src_ptrs  device array of n_params pointers to flat parameters
+ *   src_dtype   0 = fp32 sources, ZERO_BF16 / ZERO_FP16 = 16-bit sources (converted exactly)
+ *   d_p32       device float[shard_numel], 16-byte aligned */
+zero_status zero_shard_init(const zero_plan* plan, const void* const* d_src_ptrs, int32_t src_dtype, float* d_p32,
+                            void* stream);
 
 /* Thread-local text of the last error ("" if none). */
 const char* zero_last_error(void);

@@ -1,0 +1,20 @@
+"""ZeRO-1/2 per-rank shard pipeline for one MI355X (gfx950).
+
+The C ABI (include/zero_shard.h) is implemented by hand-written HIP kernels in csrc/ and
+built in place into libzero_shard.so; this package exposes the same entry points over
+torch device tensors.  PyTorch provides device memory and streams only.
+"""
+from ._binding import (EXPORTS, LIB_PATH, ZERO_BF16, ZERO_EHIP, ZERO_EINVAL, ZERO_ENOMEM, ZERO_ERANGE, ZERO_FP16,
+                       ZERO_OK, Plan, ZeroError, lib, ptr_table, zero_adam_step, zero_bucket_info, zero_last_error,
+                       zero_model_state_bytes, zero_overflow_check, zero_pack_bucket, zero_param_info,
+                       zero_plan_bucket_info, zero_plan_create, zero_plan_destroy, zero_plan_get_summary,
+                       zero_plan_model_state_bytes, zero_plan_param_info, zero_plan_summary, zero_reduce_shard,
+                       zero_shard_init, zero_unpack)
+from .step import ShardStep
+
+__all__ = ["EXPORTS", "LIB_PATH", "Plan", "ShardStep", "ZeroError", "lib", "ptr_table", "zero_adam_step",
+           "zero_last_error", "zero_model_state_bytes", "zero_overflow_check", "zero_pack_bucket",
+           "zero_plan_bucket_info", "zero_plan_create", "zero_plan_destroy", "zero_plan_get_summary",
+           "zero_plan_model_state_bytes", "zero_plan_param_info", "zero_reduce_shard", "zero_shard_init",
+           "zero_unpack", "ZERO_BF16", "ZERO_FP16", "ZERO_OK", "ZERO_EINVAL", "ZERO_ENOMEM", "ZERO_EHIP",
+           "ZERO_ERANGE"]

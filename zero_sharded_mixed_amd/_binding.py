@@ -1,0 +1,219 @@
+"""ctypes binding of libzero_shard.so — argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/zero_shard.h) and
+does nothing but turn torch tensors into device pointers, pick the stream and raise on a
+non-zero status.  All arithmetic of the shard pipeline runs in the HIP kernels; there is no
+CPU fallback: if the library is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
+
+ZERO_OK, ZERO_EINVAL, ZERO_ENOMEM, ZERO_EHIP, ZERO_ERANGE = 0, -1, -2, -3, -4
+ZERO_BF16, ZERO_FP16 = 1, 2
+STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_ENOMEM", -3: "ZERO_EHIP", -4: "ZERO_ERANGE"}
+
+# Every symbol the header declares (checked against the header by the ABI test).
+EXPORTS = ("zero_plan_create", "zero_plan_destroy", "zero_plan_get_summary", "zero_plan_param_info",
+           "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes", "zero_pack_bucket",
+           "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack", "zero_shard_init",
+           "zero_last_error")
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class zero_param_info(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int64) for f in ("numel", "pad", "padded_numel", "shard_size", "shard_start", "shard_end",
+                                             "shard_offset", "bucket", "bucket_col")]
+
+
+class zero_bucket_info(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int64) for f in ("first_param", "n_params", "row_elems", "row_stride", "shard_base",
+                                             "block_offset")]
+
+
+class zero_plan_summary(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int64) for f in ("n_params", "nd", "rank", "n_buckets", "shard_numel", "shard_elems",
+                                             "numel_total", "padded_total", "bucket_elems", "arena_numel")] + \
+               [("dtype", ctypes.c_int32), ("device", ctypes.c_int32)]
+
+
+class zero_adam_hparams(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_double) for f in ("lr", "beta1", "beta2", "eps", "grad_scale")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzero_shard.so (built in place by zero_sharded_mixed_amd/build.py)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: the HIP library is not built "
+                           "(python zero_sharded_mixed_amd/build.py); there is no fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+    sigs = {
+        "zero_plan_create": (i32, [vp, i64, i32, i32, i64, i32, ctypes.POINTER(vp)]),
+        "zero_plan_destroy": (None, [vp]),
+        "zero_plan_get_summary": (i32, [vp, ctypes.POINTER(zero_plan_summary)]),
+        "zero_plan_param_info": (i32, [vp, i64, ctypes.POINTER(zero_param_info)]),
+        "zero_plan_bucket_info": (i32, [vp, i64, ctypes.POINTER(zero_bucket_info)]),
+        "zero_model_state_bytes": (i32, [dbl, dbl, i32, ctypes.POINTER(dbl)]),
+        "zero_plan_model_state_bytes": (i32, [vp, i32, ctypes.POINTER(dbl)]),
+        "zero_pack_bucket": (i32, [vp, i64, vp, vp, vp]),
+        "zero_reduce_shard": (i32, [vp, i64, vp, i64, vp, vp, vp, vp]),
+        "zero_overflow_check": (i32, [vp, vp, vp, vp, vp]),
+        "zero_adam_step": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
+        "zero_unpack": (i32, [vp, i64, vp, vp, vp]),
+        "zero_shard_init": (i32, [vp, vp, i32, vp, vp]),
+        "zero_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != ZERO_OK:
+        raise ZeroError(status, lib().zero_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def ptr_table(tensors: Sequence[Optional[torch.Tensor]], device=None) -> torch.Tensor:
+    """Device int64 array of the tensors' data pointers (0 for None): a pointer table."""
+    ptrs = [0 if t is None else _ptr(t) for t in tensors]
+    return torch.tensor(ptrs, dtype=torch.int64, device=device or "cuda")
+
+
+class Plan:
+    """Owns a zero_plan*; destroyed with the object (or by close())."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if not self._h:
+            raise ValueError("plan is closed")
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            lib().zero_plan_destroy(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def zero_plan_create(numels: Sequence[int], nd: int, rank: int, bucket_bytes: int, dtype: int) -> Plan:
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
+    out = ctypes.c_void_p()
+    _check(lib().zero_plan_create(arr, len(numels), nd, rank, bucket_bytes, dtype, ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def zero_plan_destroy(plan: Plan) -> None:
+    plan.close()
+
+
+def zero_plan_get_summary(plan: Plan) -> zero_plan_summary:
+    s = zero_plan_summary()
+    _check(lib().zero_plan_get_summary(plan.handle, ctypes.byref(s)))
+    return s
+
+
+def zero_plan_param_info(plan: Plan, i: int) -> zero_param_info:
+    s = zero_param_info()
+    _check(lib().zero_plan_param_info(plan.handle, i, ctypes.byref(s)))
+    return s
+
+
+def zero_plan_bucket_info(plan: Plan, b: int) -> zero_bucket_info:
+    s = zero_bucket_info()
+    _check(lib().zero_plan_bucket_info(plan.handle, b, ctypes.byref(s)))
+    return s
+
+
+def zero_model_state_bytes(psi: float, nd: float, stage: int) -> float:
+    out = ctypes.c_double()
+    _check(lib().zero_model_state_bytes(psi, nd, stage, ctypes.byref(out)))
+    return out.value
+
+
+def zero_plan_model_state_bytes(plan: Plan, stage: int) -> float:
+    out = ctypes.c_double()
+    _check(lib().zero_plan_model_state_bytes(plan.handle, stage, ctypes.byref(out)))
+    return out.value
+
+
+def zero_pack_bucket(plan: Plan, b: int, grad_ptrs: torch.Tensor, packed: torch.Tensor, stream=None) -> None:
+    _check(lib().zero_pack_bucket(plan.handle, b, _ptr(grad_ptrs), _ptr(packed), _stream(stream)))
+
+
+def zero_reduce_shard(plan: Plan, b: int, rows: torch.Tensor, row_stride: int, live: torch.Tensor,
+                      g32: torch.Tensor, flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """rows: 16-bit device tensor whose start is row 0; row k starts k*row_stride elements in."""
+    _check(lib().zero_reduce_shard(plan.handle, b, _ptr(rows), row_stride, _ptr(live), _ptr(g32), _ptr(flag),
+                                   _stream(stream)))
+
+
+def zero_overflow_check(plan: Plan, g32: torch.Tensor, live: torch.Tensor, flag: torch.Tensor, stream=None) -> None:
+    _check(lib().zero_overflow_check(plan.handle, _ptr(g32), _ptr(live), _ptr(flag), _stream(stream)))
+
+
+def zero_adam_step(plan: Plan, g32: torch.Tensor, p32: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                   live: torch.Tensor, steps: torch.Tensor, lr: float, beta1: float, beta2: float, eps: float,
+                   grad_scale: float, flag: Optional[torch.Tensor], arena: torch.Tensor, stream=None) -> None:
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale)
+    _check(lib().zero_adam_step(plan.handle, _ptr(g32), _ptr(p32), _ptr(m), _ptr(v), _ptr(live), _ptr(steps),
+                                ctypes.byref(hp), _ptr(flag), _ptr(arena), _stream(stream)))
+
+
+def zero_unpack(plan: Plan, b: int, gathered: torch.Tensor, param_ptrs: torch.Tensor, stream=None) -> None:
+    _check(lib().zero_unpack(plan.handle, b, _ptr(gathered), _ptr(param_ptrs), _stream(stream)))
+
+
+def zero_shard_init(plan: Plan, src_ptrs: torch.Tensor, src_dtype: int, p32: torch.Tensor, stream=None) -> None:
+    _check(lib().zero_shard_init(plan.handle, _ptr(src_ptrs), src_dtype, _ptr(p32), _stream(stream)))
+
+
+def zero_last_error() -> str:
+    return lib().zero_last_error().decode(errors="replace")

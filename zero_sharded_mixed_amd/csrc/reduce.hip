@@ -1,0 +1,132 @@
+// reduce.hip — the Nd-way shard reduce (the arithmetic of the ZeRO-2 reduce-scatter of the
+// per-rank flat chunks, ColossalAI issue "[zero] improving compatibility of low level zero",
+// BWD; the bucketed reduce-scatter of stage Pos+g in the upskillscore ZeRO summary) and the
+// inf/NaN overflow check.
+//
+// Each thread owns 8 consecutive columns of the bucket row and keeps 8 fp32 accumulators.
+// It reads the 16 bytes of every rank's row at those columns (aligned dwordx4: rows start on
+// 16-byte boundaries), converts exactly to fp32 and adds in ascending rank order, seeded with
+// rank 0's value — the fixed order that makes the sums bit-reproducible.  Loads of the next
+// ranks are issued ahead of the adds (kAhead rows in flight) so HBM latency overlaps.
+// Columns of parameters without a gradient are skipped before any row is read.
+#include "zs_common.h"
+
+namespace zs {
+
+constexpr int kAhead = 8;
+
+// Bit t of the result is set when column x + t belongs to a live parameter.
+__device__ __forceinline__ unsigned live_mask8(const DevPlan& P, const uint8_t* __restrict__ live, int64_t x,
+                                               int64_t i) {
+    if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) return live[i] ? 0xffu : 0u;
+    unsigned m = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int64_t xt = x + t;
+        while (i < P.n && P.end[i] <= xt) ++i;
+        if (i < P.n && P.off[i] <= xt && live[i]) m |= 1u << t;
+    }
+    return m;
+}
+
+__device__ __forceinline__ void flag_if_bad(const float (&v)[8], unsigned mask, int32_t* flag) {
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) bad |= ((mask >> t) & 1u) && non_finite(v[t]);
+    if (bad) atomicOr(flag, 1);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_base, int64_t b_row, int64_t tile0,
+                                                        int64_t n_tile, const uint16_t* __restrict__ rows,
+                                                        int64_t row_stride, const uint8_t* __restrict__ live,
+                                                        float* __restrict__ g32, int32_t* __restrict__ flag) {
+    const int64_t nd = P.nd;
+    for (int64_t w = blockIdx.x; w < n_tile; w += gridDim.x) {
+        const int64_t x = ((tile0 + w) << kTileShift) + int64_t(threadIdx.x) * kChunk;
+        const int64_t c = x - b_base;
+        if (c < 0 || c >= b_row) continue;  // outside the bucket, or entirely in the row gap
+        const unsigned mask = live_mask8(P, live, x, param_of_column(P, x));
+        if (mask == 0) continue;
+        const uint16_t* src = rows + c;
+        float acc[8];
+        accumulate8<DT, true>(acc, *reinterpret_cast<const uint4*>(src));
+        int64_t k = 1;
+        for (; k + kAhead <= nd; k += kAhead) {
+            uint4 v[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) v[u] = *reinterpret_cast<const uint4*>(src + (k + u) * row_stride);
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
+        }
+        for (; k < nd; ++k) accumulate8<DT, false>(acc, *reinterpret_cast<const uint4*>(src + k * row_stride));
+        float* dst = g32 + x;
+        if (mask == 0xffu) {
+            reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                if (mask & (1u << t)) dst[t] = acc[t];
+        }
+        if (flag) flag_if_bad(acc, mask, flag);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,
+                                                          const uint8_t* __restrict__ live, int32_t* __restrict__ flag) {
+    for (int64_t j = blockIdx.x; j < P.n_tiles; j += gridDim.x) {
+        const int64_t x = (j << kTileShift) + int64_t(threadIdx.x) * kChunk;
+        if (x >= P.shard_numel) continue;
+        const unsigned mask = live_mask8(P, live, x, param_of_column(P, x));
+        if (mask == 0) continue;
+        const float4 a = reinterpret_cast<const float4*>(g32 + x)[0];
+        const float4 b = reinterpret_cast<const float4*>(g32 + x)[1];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        flag_if_bad(v, mask, flag);
+    }
+}
+
+}  // namespace zs
+
+using namespace zs;
+
+extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const void* d_rows, int64_t row_stride,
+                                         const uint8_t* d_live, float* d_g32, int32_t* d_flag, void* stream) {
+    zero_status st = check_device(plan);
+    if (st != ZERO_OK) return st;
+    if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "zero_reduce_shard: bucket %lld out of range", (long long)b);
+    if (!d_rows || !d_live || !d_g32) return fail(ZERO_EINVAL, "zero_reduce_shard: NULL pointer");
+    if (!host_aligned16(d_rows) || !host_aligned16(d_g32))
+        return fail(ZERO_EINVAL, "zero_reduce_shard: rows and g32 must be 16-byte aligned");
+    const int64_t* br = plan->h_bucket + b * kBucketFields;
+    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
+    if (row_stride < stride || row_stride % kChunk != 0)
+        return fail(ZERO_EINVAL, "zero_reduce_shard: row_stride %lld must be >= %lld and a multiple of 8",
+                    (long long)row_stride, (long long)stride);
+    if (row == 0) return ZERO_OK;
+    const int64_t tile0 = base >> kTileShift;
+    const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
+    const int g = grid_for(n_tile, 8192);
+    hipStream_t s = (hipStream_t)stream;
+    const uint16_t* rows = static_cast<const uint16_t*>(d_rows);
+    if (plan->dtype == ZERO_BF16)
+        reduce_kernel<ZERO_BF16><<<g, kBlock, 0, s>>>(plan->dev, base, row, tile0, n_tile, rows, row_stride, d_live,
+                                                      d_g32, d_flag);
+    else
+        reduce_kernel<ZERO_FP16><<<g, kBlock, 0, s>>>(plan->dev, base, row, tile0, n_tile, rows, row_stride, d_live,
+                                                      d_g32, d_flag);
+    return check_launch("zero_reduce_shard");
+}
+
+extern "C" zero_status zero_overflow_check(const zero_plan* plan, const float* d_g32, const uint8_t* d_live,
+                                           int32_t* d_flag, void* stream) {
+    zero_status st = check_device(plan);
+    if (st != ZERO_OK) return st;
+    if (!d_g32 || !d_live || !d_flag) return fail(ZERO_EINVAL, "zero_overflow_check: NULL pointer");
+    if (!host_aligned16(d_g32)) return fail(ZERO_EINVAL, "zero_overflow_check: g32 not 16-byte aligned");
+    if (plan->shard_numel == 0) return ZERO_OK;
+    overflow_kernel<<<grid_for(plan->dev.n_tiles, 8192), kBlock, 0, (hipStream_t)stream>>>(plan->dev, d_g32, d_live,
+                                                                                          d_flag);
+    return check_launch("zero_overflow_check");
+}

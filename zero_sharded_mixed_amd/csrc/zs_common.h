@@ -1,0 +1,190 @@
+// zs_common.h — definitions shared by the shard-pipeline kernels and their host entry points.
+//
+// Index spaces the kernels walk (see include/zero_shard.h for the layout):
+//   * shard columns x in [0, shard_numel): rank r's flat fp32 shard.  Bucket b owns
+//     [O_b, O_b + L_b); column x of the shard is column x - O_b of every rank row of b.
+//     Parameter i owns [off_i, end_i), end_i = off_i + s_i.  end_i never decreases with i.
+//   * unpack chunks u in [0, total_chunks): parameter i owns chunks [ucb_i, ucend_i),
+//     ucend_i - ucb_i = ceil(numel_i / 8); chunk u covers its elements 8*(u - ucb_i) + 0..7.
+// Both spaces are cut into tiles; tile_first[j] is the first parameter whose range ends after
+// the tile's first column (or chunk), so the parameter owning any point of tile j is found by
+// a binary search over [tile_first[j], tile_first[j+1]] — usually a range of one or two.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_shard.h"
+
+namespace zs {
+
+constexpr int kBlock = 256;                  // threads per block in every hot kernel
+constexpr int kChunk = 8;                    // elements per thread chunk (16 bytes of 16-bit data)
+constexpr int kTileShift = 11;               // shard tile = 2048 columns = one chunk per thread
+constexpr int64_t kTileCols = int64_t(1) << kTileShift;
+constexpr int kUTileShift = 8;               // unpack tile = 256 chunks = one chunk per thread
+constexpr int64_t kUTileChunks = int64_t(1) << kUTileShift;
+constexpr int32_t kMaxNd = 65535;
+constexpr int64_t kMaxNumel = int64_t(1) << 48;
+
+// Read-only view of a plan's device tables, passed to kernels by value.
+struct DevPlan {
+    int64_t n;            // parameters
+    int64_t nd;           // ranks
+    int64_t rank;
+    int64_t shard_numel;  // sum of L_b
+    int64_t n_tiles;      // ceil(shard_numel / kTileCols)
+    int64_t n_utiles;     // ceil(total_chunks / kUTileChunks)
+    const int64_t* numel;
+    const int64_t* s;
+    const int64_t* off;
+    const int64_t* end;
+    const double* inv_s;     // 1.0 / s_i (0 when s_i == 0)
+    const int32_t* bucket;
+    const int64_t* ucb;
+    const int64_t* ucend;
+    const int64_t* b_base;   // O_b
+    const int64_t* b_stride; // L_b
+    const int64_t* b_row;    // S_b
+    const int32_t* tile_first;   // [n_tiles + 1]
+    const int32_t* utile_first;  // [n_utiles + 1]
+};
+
+// First index i in [lo, hi] with key[i] > x, given key non-decreasing and key[hi] > x
+// (or hi == n).  Returns hi when none before it qualifies.
+__device__ __forceinline__ int64_t first_greater(const int64_t* __restrict__ key, int64_t lo, int64_t hi, int64_t x) {
+    while (lo < hi) {
+        int64_t mid = (lo + hi) >> 1;
+        if (key[mid] > x) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+// Parameter whose shard range could hold column x: the first i with end_i > x (n if none).
+// The caller checks off_i <= x (otherwise x lies in a row gap).
+__device__ __forceinline__ int64_t param_of_column(const DevPlan& P, int64_t x) {
+    int64_t j = x >> kTileShift;
+    return first_greater(P.end, P.tile_first[j], P.tile_first[j + 1], x);
+}
+
+// Parameter owning unpack chunk u (first i with ucend_i > u).
+__device__ __forceinline__ int64_t param_of_chunk(const DevPlan& P, int64_t u) {
+    int64_t j = u >> kUTileShift;
+    return first_greater(P.ucend, P.utile_first[j], P.utile_first[j + 1], u);
+}
+
+// Eight consecutive 16-bit elements starting at element e of a 16-byte aligned buffer,
+// assembled from the aligned 16-byte granules that hold them.  Never touches a granule that
+// holds none of the eight elements.
+__device__ __forceinline__ uint4 load8_realigned(const uint16_t* __restrict__ base, int64_t e) {
+    const uint4* v = reinterpret_cast<const uint4*>(base);
+    const int64_t q = e >> 3;
+    const int d = int(e & 7);
+    const uint4 a = v[q];
+    if (d == 0) return a;
+    const uint4 b = v[q + 1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint4 r;
+    switch (d) {  // word shift by d/2, then a 2-byte shift when d is odd
+        case 1: r = make_uint4(__builtin_amdgcn_alignbyte(w[1], w[0], 2), __builtin_amdgcn_alignbyte(w[2], w[1], 2),
+                               __builtin_amdgcn_alignbyte(w[3], w[2], 2), __builtin_amdgcn_alignbyte(w[4], w[3], 2)); break;
+        case 2: r = make_uint4(w[1], w[2], w[3], w[4]); break;
+        case 3: r = make_uint4(__builtin_amdgcn_alignbyte(w[2], w[1], 2), __builtin_amdgcn_alignbyte(w[3], w[2], 2),
+                               __builtin_amdgcn_alignbyte(w[4], w[3], 2), __builtin_amdgcn_alignbyte(w[5], w[4], 2)); break;
+        case 4: r = make_uint4(w[2], w[3], w[4], w[5]); break;
+        case 5: r = make_uint4(__builtin_amdgcn_alignbyte(w[3], w[2], 2), __builtin_amdgcn_alignbyte(w[4], w[3], 2),
+                               __builtin_amdgcn_alignbyte(w[5], w[4], 2), __builtin_amdgcn_alignbyte(w[6], w[5], 2)); break;
+        case 6: r = make_uint4(w[3], w[4], w[5], w[6]); break;
+        default: r = make_uint4(__builtin_amdgcn_alignbyte(w[4], w[3], 2), __builtin_amdgcn_alignbyte(w[5], w[4], 2),
+                                __builtin_amdgcn_alignbyte(w[6], w[5], 2), __builtin_amdgcn_alignbyte(w[7], w[6], 2)); break;
+    }
+    return r;
+}
+
+__device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+__device__ __forceinline__ uint16_t elem_of(const uint4& v, int t) {
+    const uint32_t w = t < 2 ? v.x : t < 4 ? v.y : t < 6 ? v.z : v.w;
+    return uint16_t((t & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+__device__ __forceinline__ uint4 pack8(const uint16_t (&h)[8]) {
+    return make_uint4(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16),
+                      uint32_t(h[4]) | (uint32_t(h[5]) << 16), uint32_t(h[6]) | (uint32_t(h[7]) << 16));
+}
+
+// Exact 16-bit -> fp32 conversions.  DT is a zero_dtype.
+template <int DT>
+__device__ __forceinline__ float to_f32(uint32_t h) {
+    if constexpr (DT == ZERO_BF16) {
+        return __uint_as_float(h << 16);
+    } else {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+    }
+}
+
+// Convert the eight 16-bit values of v and add them, in order, into acc (or set acc).
+template <int DT, bool kFirst>
+__device__ __forceinline__ void accumulate8(float (&acc)[8], const uint4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float lo = to_f32<DT>(w[t] & 0xffffu);
+        const float hi = to_f32<DT>(w[t] >> 16);
+        if constexpr (kFirst) {
+            acc[2 * t] = lo;
+            acc[2 * t + 1] = hi;
+        } else {
+            acc[2 * t] = acc[2 * t] + lo;
+            acc[2 * t + 1] = acc[2 * t + 1] + hi;
+        }
+    }
+}
+
+// fp32 -> 16-bit, round to nearest even (finite inputs; NaN becomes a quiet NaN).
+template <int DT>
+__device__ __forceinline__ uint16_t from_f32(float f) {
+    if constexpr (DT == ZERO_BF16) {
+        const uint32_t u = __float_as_uint(f);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t(((u >> 16) & 0x8000u) | 0x7fc0u);
+        return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    } else {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+    }
+}
+
+__device__ __forceinline__ bool non_finite(float f) { return (__float_as_uint(f) & 0x7f800000u) == 0x7f800000u; }
+
+}  // namespace zs
+
+// Host side: the opaque plan.
+struct zero_plan {
+    int64_t n = 0, nd = 0, rank = 0, n_buckets = 0, shard_numel = 0, shard_elems = 0;
+    int64_t numel_total = 0, padded_total = 0, bucket_elems = 0, total_chunks = 0;
+    int32_t dtype = 0, device = 0;
+    // host copies, one row per parameter / bucket
+    int64_t* h_param = nullptr;   // n * kParamFields
+    int64_t* h_bucket = nullptr;  // n_buckets * kBucketFields
+    int64_t* h_bucket_chunks = nullptr;  // [n_buckets][2]: the bucket's unpack chunk range [u0, u1)
+    // device tables
+    void* d_mem = nullptr;        // one allocation holding every table below
+    zs::DevPlan dev{};
+    int32_t* d_bfirst = nullptr;
+    int32_t* d_bcount = nullptr;
+    float* d_adam_scal = nullptr; // [n][2] per-parameter step size and 1/sqrt(bias correction 2)
+    float* d_adam_const = nullptr;// [8] fp32 hyperparameters formed on the device
+};
+
+namespace zs {
+enum ParamField { PF_NUMEL, PF_PAD, PF_PADDED, PF_SHARD, PF_START, PF_END, PF_OFFSET, PF_BUCKET, PF_COL, kParamFields };
+enum BucketField { BF_FIRST, BF_COUNT, BF_ROW, BF_STRIDE, BF_BASE, kBucketFields };
+
+// Thread-local error text and status helpers (defined in plan.hip).
+zero_status fail(zero_status st, const char* fmt, ...);
+zero_status check_launch(const char* what);
+zero_status check_device(const zero_plan* plan);
+inline bool host_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+inline int grid_for(int64_t work, int64_t cap = 4096) {
+    return int(work < 1 ? 1 : (work < cap ? work : cap));
+}
+}  // namespace zs

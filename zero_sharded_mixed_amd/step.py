@@ -1,0 +1,82 @@
+"""One rank's shard step, driven through the C ABI: pack -> reduce (+ overflow flag) -> Adam
+-> unpack, the order of the ZeRO-1 sequence on the briefia.fr page ("ZeRO-1 : Partitionnement
+des états de l'optimiseur": gradients synchronised, own partition stepped, parameters
+all-gathered) with the ZeRO-2 reduce-scatter of the ColossalAI "low level zero" issue (BWD).
+
+This class only allocates the rank's device buffers (sizes read from the plan) and issues the
+entry points in order on one stream; every element of work runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional, Sequence
+
+import torch
+
+from . import _binding as B
+
+
+class ShardStep:
+    def __init__(self, numels: Sequence[int], nd: int, rank: int, bucket_bytes: int, dtype: int, device="cuda"):
+        self.device = torch.device(device)
+        self.plan = B.zero_plan_create(numels, nd, rank, bucket_bytes, dtype)
+        self.summary = B.zero_plan_get_summary(self.plan)
+        s = self.summary
+        self.nd, self.rank, self.dtype = nd, rank, dtype
+        self.n = int(s.n_params)
+        self.buckets = [B.zero_plan_bucket_info(self.plan, b) for b in range(int(s.n_buckets))]
+        S = int(s.shard_numel)
+        f32 = dict(dtype=torch.float32, device=self.device)
+        self.p32 = torch.zeros(S, **f32)
+        self.m = torch.zeros(S, **f32)
+        self.v = torch.zeros(S, **f32)
+        self.g32 = torch.zeros(S, **f32)
+        self.steps = torch.zeros(self.n, dtype=torch.int32, device=self.device)
+        self.live = torch.ones(self.n, dtype=torch.uint8, device=self.device)
+        self.flag = torch.zeros(1, dtype=torch.int32, device=self.device)
+        # this rank's packed gradient buckets and the all-gather arena share one layout:
+        # bucket b's [Nd][L_b] block starts at block_offset
+        self.packed = torch.zeros(int(s.arena_numel), dtype=torch.int16, device=self.device)
+        self.arena = torch.zeros(int(s.arena_numel), dtype=torch.int16, device=self.device)
+
+    # -- views ---------------------------------------------------------------------------
+    def block(self, buf: torch.Tensor, b: int) -> torch.Tensor:
+        bk = self.buckets[b]
+        return buf[bk.block_offset:bk.block_offset + self.nd * bk.row_stride]
+
+    def own_row(self, buf: torch.Tensor, b: int, k: Optional[int] = None) -> torch.Tensor:
+        bk = self.buckets[b]
+        k = self.rank if k is None else k
+        start = bk.block_offset + k * bk.row_stride
+        return buf[start:start + bk.row_stride]
+
+    # -- the steps -----------------------------------------------------------------------
+    def init_master(self, src_ptrs: torch.Tensor, src_dtype: int = 0, stream=None) -> None:
+        B.zero_shard_init(self.plan, src_ptrs, src_dtype, self.p32, stream)
+
+    def pack(self, grad_ptrs: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> None:
+        out = self.packed if out is None else out
+        for b in range(len(self.buckets)):
+            B.zero_pack_bucket(self.plan, b, grad_ptrs, self.block(out, b), stream)
+
+    def reduce(self, rows_of: Callable[[int], tuple], fused_check: bool = True, stream=None) -> None:
+        """rows_of(b) -> (tensor starting at row 0 of bucket b, row stride in elements)."""
+        for b in range(len(self.buckets)):
+            rows, stride = rows_of(b)
+            B.zero_reduce_shard(self.plan, b, rows, stride, self.live, self.g32,
+                                self.flag if fused_check else None, stream)
+
+    def overflow_check(self, stream=None) -> None:
+        B.zero_overflow_check(self.plan, self.g32, self.live, self.flag, stream)
+
+    def adam(self, lr: float, beta1: float, beta2: float, eps: float, grad_scale: float, use_flag: bool = True,
+             stream=None) -> None:
+        B.zero_adam_step(self.plan, self.g32, self.p32, self.m, self.v, self.live, self.steps, lr, beta1, beta2,
+                         eps, grad_scale, self.flag if use_flag else None, self.arena, stream)
+
+    def unpack(self, param_ptrs: torch.Tensor, src: Optional[torch.Tensor] = None, stream=None) -> None:
+        src = self.arena if src is None else src
+        for b in range(len(self.buckets)):
+            B.zero_unpack(self.plan, b, self.block(src, b), param_ptrs, stream)
+
+    def close(self) -> None:
+        self.plan.close()
