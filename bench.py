@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Shard-step throughput of the ZeRO-1/2 per-rank pipeline on one MI355X.
+
+One step = every hot-path stage for one rank over one batch of synthetic gradients:
+pack this rank's gradient buckets rank-major, reduce the Nd virtual ranks' rows into the fp32
+shard (overflow flag fused), the fused mixed-precision Adam step writing the 16-bit all-gather
+row, and the unpack of the gathered buckets into the per-parameter flats.  The default
+workload is a GPT-2 1.5B-shaped parameter list at Nd = 8 virtual ranks, rank 0, 500M-element
+buckets, bf16 gradients and parameters, fp32 master / momentum / variance, with the other
+virtual ranks' gradients packed beforehand (their rows are what a reduce-scatter would
+deliver).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0).  value = algorithmic HBM bytes of the step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import zero_sharded_mixed_amd as Z  # noqa: E402  (fails at first call if the HIP library is missing)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "shard step GB/s & elem/s (pack+reduce+Adam) vs HBM peak, 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(numels, shard_sizes, live, nd):
+    """Bytes each stage must move, per the method (not what the kernels happen to move):
+    pack 2 B read per gradient element + 2 B written per padded element; reduce Nd 16-bit
+    reads + one fp32 write per shard element; Adam 16 B read (g, p, m, v) + 14 B written
+    (p, m, v, 16-bit param) per shard element; unpack 2 B read + 2 B written per element."""
+    numel_live = int(sum(int(n) for n, l in zip(numels, live) if l))
+    padded_live = int(sum(int(s) * nd for s, l in zip(shard_sizes, live) if l))
+    shard_live = int(sum(int(s) for s, l in zip(shard_sizes, live) if l))
+    numel_all = int(sum(int(n) for n in numels))
+    return {
+        "pack": 2 * numel_live + 2 * padded_live,
+        "reduce": (2 * nd + 4) * shard_live,
+        "adam": 30 * shard_live,
+        "unpack": 4 * numel_all,
+        "shard_live": shard_live,
+        "numel_live": numel_live,
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "zero_sharded_mixed_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- GPU side --
+
+def setup_gpu(w, device):
+    import workloads as W
+
+    torch.cuda.set_device(device)
+    t0 = time.time()
+    st = Z.ShardStep(w.numels, w.nd, w.rank, w.bucket_bytes, w.dtype, device=device)
+    s = st.summary
+    log(f"[bench] plan: n={s.n_params} nd={s.nd} rank={s.rank} buckets={s.n_buckets} shard={s.shard_numel} "
+        f"psi={s.padded_total} ({time.time() - t0:.1f}s)")
+    masters = W.masters(w, device)
+    st.init_master(Z.ptr_table(masters), 0)
+    lp = [m.to(torch.bfloat16 if w.dtype == W.BF16 else torch.float16) for m in masters]
+    del masters
+    lp_ptrs = Z.ptr_table(lp)
+    st.pack(lp_ptrs, out=st.arena)  # every rank holds the full model: the gathered rows start equal
+    live = W.live_mask(w, 0)
+    st.live.copy_(torch.from_numpy(live))
+    # every virtual rank's packed gradients; rank r's are re-packed inside each timed step
+    packed_all = torch.empty((w.nd, int(s.arena_numel)), dtype=torch.int16, device=device)
+    own = None
+    for k in range(w.nd):
+        g = W.grads(w, 0, k, device)
+        gl = [t if l else None for t, l in zip(g, live)]
+        ptrs = Z.ptr_table(gl)
+        st.pack(ptrs, out=packed_all[k])
+        if k == w.rank:
+            own = (gl, ptrs)
+        else:
+            del gl, g
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB ({time.time() - t0:.1f}s)")
+    flat = packed_all.view(-1)
+    stride = int(s.arena_numel)
+
+    def rows_of(b):
+        bk = st.buckets[b]
+        return flat[bk.block_offset + w.rank * bk.row_stride:], stride
+
+    return st, own, packed_all, rows_of, lp, lp_ptrs, live
+
+
+def run_gpu(w, steps, warmup, device):
+    st, own, packed_all, rows_of, lp, lp_ptrs, live = setup_gpu(w, device)
+    _, own_ptrs = own
+    own_out = packed_all[w.rank]
+    b1, b2 = w.betas
+    phases = ("pack", "reduce", "adam", "unpack")
+
+    def one_step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        st.pack(own_ptrs, out=own_out)
+        if ev is not None:
+            ev[1].record()
+        st.flag.zero_()
+        st.reduce(rows_of, fused_check=True)
+        if ev is not None:
+            ev[2].record()
+        st.adam(w.lr, b1, b2, w.eps, w.grad_scale)
+        if ev is not None:
+            ev[3].record()
+        st.unpack(lp_ptrs)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_phase = {p: 0.0 for p in phases}
+    for ev in events:
+        for j, p in enumerate(phases):
+            per_phase[p] += ev[j].elapsed_time(ev[j + 1])
+    per_phase = {p: v / steps for p, v in per_phase.items()}  # ms per step
+    launches = {"pack": len(st.buckets), "reduce": len(st.buckets), "adam": 2, "unpack": len(st.buckets)}
+    shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
+    flag = int(st.flag.item())
+    return wall / steps * 1e3, per_phase, launches, shard_sizes, flag
+
+
+# --------------------------------------------------------------------------- CPU side --
+
+def cpu_baseline(w, max_elems: int):
+    """The oracle, single-threaded, on a prefix of the same parameter list (the whole step:
+    pack, reduce, overflow, Adam, unpack), inputs drawn from the same distributions."""
+    import oracle
+    import workloads as W
+
+    numels = w.numels
+    keep = 1
+    while keep < len(numels) and numels[:keep + 1].sum() <= max_elems:
+        keep += 1
+    sub = numels[:keep]
+    pl = oracle.plan(sub, w.nd, w.rank, w.bucket_bytes)
+    # values drawn on the device (fast) from the workload's distributions, copied to the host
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(W.seed_of(w.config, 0, 0, W.SLOT_GRAD))
+    tdt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
+
+    def bits16(n, std):
+        x = torch.randn(n, generator=gen, device="cuda") * std
+        return x.to(tdt).view(torch.int16).cpu().numpy().view(np.uint16)
+
+    grads = [bits16(int(x), w.grad_std) for x in sub]
+    S = pl.shard_len
+    rows = [bits16(w.nd * int(pl.buckets[b, oracle.B_STRIDE]), w.grad_std).reshape(w.nd, -1)
+            for b in range(pl.n_buckets)]
+    p32 = (torch.randn(S, generator=gen, device="cuda") * w.master_std).cpu().numpy()
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    g32 = np.zeros(S, np.float32)
+    steps = np.zeros(pl.n, np.int32)
+    arena = np.zeros(w.nd * S, np.uint16)
+    live = np.ones(pl.n, np.uint8)
+    outs = [np.empty(int(x), np.uint16) for x in sub]
+    hp = oracle.AdamHP(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps, grad_scale=w.grad_scale)
+    t0 = time.perf_counter()
+    for b in range(pl.n_buckets):
+        oracle.pack_bucket(pl, b, grads)
+    for b in range(pl.n_buckets):
+        oracle.reduce_bucket(pl, b, rows[b], w.dtype, live, g32)
+    flag = oracle.overflow(pl, g32, live)
+    oracle.adam(pl, g32, p32, m, v, live, steps, hp, flag, arena, w.dtype)
+    for b in range(pl.n_buckets):
+        base = w.nd * int(pl.buckets[b, oracle.B_BASE])
+        L = int(pl.buckets[b, oracle.B_STRIDE])
+        oracle.unpack_bucket(pl, b, arena[base:base + w.nd * L].reshape(w.nd, L), outs)
+    secs = time.perf_counter() - t0
+    ab = algorithmic_bytes(sub, pl.params[:, oracle.P_SHARD], live, w.nd)
+    total = ab["pack"] + ab["reduce"] + ab["adam"] + ab["unpack"]
+    names = [n for n, _ in w.params[:keep]]
+    return {"value": round(total / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(secs, 2), "elem_per_s": round(ab["shard_live"] / secs, 1),
+            "sample": f"first {keep} of {len(numels)} parameters ({names[0]} .. {names[-1]}), "
+                      f"{int(sub.sum())} elements, one full step (pack, reduce, overflow, Adam, unpack), "
+                      f"single thread, plain C oracle"}
+
+
+# -------------------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload: 2 = GPT-2 1.5B-shaped list (default)")
+    ap.add_argument("--cpu-sample-elems", type=int, default=800_000_000,
+                    help="oracle sample: the longest prefix of the parameter list with at most this many elements")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU reduce-scatter/all-gather path is not built)", file=sys.stderr)
+        sys.exit(2)
+    if args.config != 2:
+        print("bench.py: only the default workload (--config 2, GPT-2 1.5B-shaped list) is timed", file=sys.stderr)
+        sys.exit(2)
+    import workloads as W
+
+    w = W.workload(args.config)
+    device = torch.device("cuda:0")
+    ms, per_phase, launches, shard_sizes, flag = run_gpu(w, args.steps, args.warmup, device)
+    live = W.live_mask(w, 0)
+    ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
+    step_bytes = ab["pack"] + ab["reduce"] + ab["adam"] + ab["unpack"]
+    kernels = {}
+    for p in ("pack", "reduce", "adam", "unpack"):
+        kernels[p] = {"ms": round(per_phase[p], 4), "launches": launches[p], "bytes": ab[p],
+                      "GBs": round(ab[p] / (per_phase[p] * 1e-3) / 1e9, 1),
+                      "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    dom = max(kernels, key=lambda p: kernels[p]["ms"])
+    workload = "gpt2-1.5b-nd8-r0"
+    traffic = measured_traffic(dom, workload)
+    d = kernels[dom]
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "GPT-2 1.5B-shaped parameter list (48 layers, d=1600, vocab 50257, 1024 positions); "
+                               "Nd=8 virtual ranks, rank 0, 500M-element buckets; bf16 grads N(0,1e-3) and params, "
+                               "fp32 master N(0,0.02) / m / v; Adam lr 1e-3, betas (0.9, 0.999), eps 1e-8",
+                   "workload_id": workload, "nd": w.nd, "rank": w.rank, "n_params": w.n,
+                   "psi": int(sum(s * w.nd for s in shard_sizes)), "shard_elems": ab["shard_live"],
+                   "n_buckets": launches["pack"], "storage": "bf16 grads/params, fp32 state"},
+        "elem_per_s": round(ab["shard_live"] / (ms * 1e-3), 1),
+        "grad_elem_per_s": round(ab["numel_live"] / (ms * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "overflow_flag": flag,
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["bytes"] / launches[dom] /
+                                                                      (d["ms"] / launches[dom] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
+                     "traffic": traffic, "bytes_per_launch": d["bytes"] // launches[dom],
+                     "avg_launch_ms": round(d["ms"] / launches[dom], 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host (cpu_baseline) ...")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_elems)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
