@@ -168,6 +168,24 @@ def run_gpu(w, steps, warmup, device):
     return wall / steps * 1e3, per_phase, launches, shard_sizes, flag
 
 
+def copy_reference(device, nbytes=2 << 30, reps=10):
+    """GB/s (read + write) of torch's device-to-device copy of a 2 GiB buffer: what a plain
+    streaming kernel reaches on this device, for context next to the 8 TB/s peak."""
+    a = torch.empty(nbytes // 2, dtype=torch.int16, device=device)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 # --------------------------------------------------------------------------- CPU side --
 
 def cpu_baseline(w, max_elems: int):
@@ -291,6 +309,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
                      "traffic": traffic, "bytes_per_launch": d["bytes"] // launches[dom],
                      "avg_launch_ms": round(d["ms"] / launches[dom], 4)},
+        "copy_reference_GBs": copy_reference(device),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

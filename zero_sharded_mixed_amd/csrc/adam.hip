@@ -13,8 +13,8 @@
 // the overflow flag, bumps the step count of every live parameter and forms its step size
 // lr / (1 - beta1^t) and 1 / sqrt(1 - beta2^t) in double, rounded to fp32 once; it also forms
 // the fp32 hyperparameters (1 - beta computed in double, then rounded).  adam_kernel then
-// streams the shard: per thread one 8-column chunk, reading g32, p32, m, v as two dwordx4
-// each and writing p32, m, v and 8 16-bit parameters (one dwordx4) — 30 bytes per element.
+// streams the shard, one block per span of kBlock * kAdamCols columns, reading g32, p32, m, v
+// and writing p32, m, v and the 16-bit parameters — 30 bytes per element.
 // Both kernels return at once when the flag is set, so a skipped step changes nothing.
 #include <cmath>
 
@@ -72,61 +72,106 @@ __device__ __forceinline__ void adam_elem(const AdamK& K, float g32, float& p, f
     p = p - step_size * (m / denom);
 }
 
-template <int DT>
-__global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A) {
+#ifndef ZS_ADAM_COLS
+#define ZS_ADAM_COLS 8
+#endif
+constexpr int kAdamCols = ZS_ADAM_COLS;  // shard columns per thread (4 or 8)
+
+template <int COLS> struct LpVec;
+template <> struct LpVec<4> { using T = uint2; };
+template <> struct LpVec<8> { using T = uint4; };
+
+// COLS consecutive columns of one live parameter: COLS/4 dwordx4 loads each of g, p, m, v;
+// COLS/4 dwordx4 stores each of p, m, v; one store of the COLS 16-bit parameters.
+template <int DT, int COLS>
+__device__ __forceinline__ void adam_cols(const AdamK& K, const AdamArgs& A, int64_t x, float2 sc, uint16_t* lp_dst) {
+    constexpr int V = COLS / 4;
+    float4 g4[V], p4[V], m4[V], v4[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+        g4[q] = load4f(A.g32 + x + 4 * q);
+        p4[q] = load4f(A.p32 + x + 4 * q);
+        m4[q] = load4f(A.m + x + 4 * q);
+        v4[q] = load4f(A.v + x + 4 * q);
+    }
+    uint16_t h[COLS];
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+        float* gq = &g4[q].x;
+        float* pq = &p4[q].x;
+        float* mq = &m4[q].x;
+        float* vq = &v4[q].x;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            adam_elem(K, gq[t], pq[t], mq[t], vq[t], sc.x, sc.y);
+            h[4 * q + t] = from_f32<DT>(pq[t]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+        store4f(A.p32 + x + 4 * q, p4[q]);
+        store4f(A.m + x + 4 * q, m4[q]);
+        store4f(A.v + x + 4 * q, v4[q]);
+    }
+    if constexpr (COLS == 8) {
+        store16(lp_dst, pack8(h));
+    } else {
+        *gptr(reinterpret_cast<uint64_t*>(lp_dst)) =
+            uint64_t(uint32_t(h[0]) | (uint32_t(h[1]) << 16)) | (uint64_t(uint32_t(h[2]) | (uint32_t(h[3]) << 16)) << 32);
+    }
+}
+
+// One block per span of kBlock * COLS shard columns.
+template <int DT, int COLS>
+__global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int64_t n_spans) {
     if (A.flag && *A.flag) return;
-    const AdamK K{A.consts[AC_BETA1], A.consts[AC_BETA2], A.consts[AC_C1],
-                  A.consts[AC_C2],    A.consts[AC_EPS],   A.consts[AC_GSCALE]};
-    for (int64_t j = blockIdx.x; j < P.n_tiles; j += gridDim.x) {
-        const int64_t x = (j << kTileShift) + int64_t(threadIdx.x) * kChunk;
+    constexpr int64_t kSpan = int64_t(kBlock) * COLS;
+    static_assert(kTileCols % kSpan == 0, "a span never crosses a tile");
+    const AdamK K{ld_const(A.consts, AC_BETA1), ld_const(A.consts, AC_BETA2), ld_const(A.consts, AC_C1),
+                  ld_const(A.consts, AC_C2),    ld_const(A.consts, AC_EPS),   ld_const(A.consts, AC_GSCALE)};
+    for (int64_t sp = blockIdx.x; sp < n_spans; sp += gridDim.x) {
+        const int64_t x0 = sp * kSpan;
+        const int64_t x = x0 + int64_t(threadIdx.x) * COLS;
+        // block-uniform (scalar loads): the whole span inside one parameter -> its scalars
+        const int64_t iu = ld_const(P.tile_first, x0 >> kTileShift);
+        const int64_t ic = iu < P.n ? iu : P.n - 1;
+        const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
+        const bool lv = ld_const(A.live, ic) != 0;
+        const float2 sc = ld_const_f2(A.scal, ic);
+        const int32_t bu = ld_const(P.bucket, ic);
+        if (iu < P.n && off <= x0 && end >= x0 + kSpan) {
+            if (!lv) continue;
+            const int64_t O = ld_const(P.b_base, bu);
+            adam_cols<DT, COLS>(K, A, x, sc, A.arena + P.nd * O + P.rank * ld_const(P.b_stride, bu) + (x - O));
+            continue;
+        }
         if (x >= P.shard_numel) continue;
         int64_t i = param_of_column(P, x);
-        if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) {
-            // Whole chunk inside live parameter i: the wide path.
+        if (i < P.n && P.off[i] <= x && x + COLS <= P.end[i]) {
+            // the thread's columns inside parameter i
             if (!A.live[i]) continue;
-            const float2 sc = A.scal[i];
             const int32_t b = P.bucket[i];
             const int64_t O = P.b_base[b];
-            const float4* gv = reinterpret_cast<const float4*>(A.g32 + x);
-            float4* pv = reinterpret_cast<float4*>(A.p32 + x);
-            float4* mv = reinterpret_cast<float4*>(A.m + x);
-            float4* vv = reinterpret_cast<float4*>(A.v + x);
-            const float4 g0 = gv[0], g1 = gv[1];
-            float4 p0 = pv[0], p1 = pv[1], m0 = mv[0], m1 = mv[1], v0 = vv[0], v1 = vv[1];
-            float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-            float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-            float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint16_t h[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                adam_elem(K, g[t], p[t], m[t], v[t], sc.x, sc.y);
-                h[t] = from_f32<DT>(p[t]);
-            }
-            pv[0] = make_float4(p[0], p[1], p[2], p[3]);
-            pv[1] = make_float4(p[4], p[5], p[6], p[7]);
-            mv[0] = make_float4(m[0], m[1], m[2], m[3]);
-            mv[1] = make_float4(m[4], m[5], m[6], m[7]);
-            vv[0] = make_float4(v[0], v[1], v[2], v[3]);
-            vv[1] = make_float4(v[4], v[5], v[6], v[7]);
-            uint16_t* dst = A.arena + P.nd * O + P.rank * P.b_stride[b] + (x - O);
-            *reinterpret_cast<uint4*>(dst) = pack8(h);
+            adam_cols<DT, COLS>(K, A, x, A.scal[i], A.arena + P.nd * O + P.rank * P.b_stride[b] + (x - O));
         } else {
-            // Chunk across parameters, dead slots or a row gap: element by element.
+            // columns across parameters, dead slots or a row gap: element by element
+            ZS_GLOBAL float* p32 = gptr(A.p32);
+            ZS_GLOBAL float* mm = gptr(A.m);
+            ZS_GLOBAL float* vv = gptr(A.v);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < COLS; ++t) {
                 const int64_t xt = x + t;
                 while (i < P.n && P.end[i] <= xt) ++i;
                 if (!(i < P.n && P.off[i] <= xt) || !A.live[i]) continue;
-                const float2 sc = A.scal[i];
+                const float2 sci = A.scal[i];
                 const int32_t b = P.bucket[i];
                 const int64_t O = P.b_base[b];
-                float p = A.p32[xt], m = A.m[xt], v = A.v[xt];
-                adam_elem(K, A.g32[xt], p, m, v, sc.x, sc.y);
-                A.p32[xt] = p;
-                A.m[xt] = m;
-                A.v[xt] = v;
-                A.arena[P.nd * O + P.rank * P.b_stride[b] + (xt - O)] = from_f32<DT>(p);
+                float p = p32[xt], m = mm[xt], v = vv[xt];
+                adam_elem(K, gptr(A.g32)[xt], p, m, v, sci.x, sci.y);
+                p32[xt] = p;
+                mm[xt] = m;
+                vv[xt] = v;
+                gptr(A.arena)[P.nd * O + P.rank * P.b_stride[b] + (xt - O)] = from_f32<DT>(p);
             }
         }
     }
@@ -157,10 +202,12 @@ extern "C" zero_status zero_adam_step(const zero_plan* plan, const float* d_g32,
     if ((st = check_launch("adam_prepare_kernel")) != ZERO_OK) return st;
     if (plan->shard_numel == 0) return ZERO_OK;
     AdamArgs A{d_g32, d_p32, d_m, d_v, d_live, scal, plan->d_adam_const, d_flag, static_cast<uint16_t*>(d_arena)};
-    const int g = grid_for(plan->dev.n_tiles, 8192);
+    const int64_t span = int64_t(kBlock) * kAdamCols;
+    const int64_t n_spans = (plan->shard_numel + span - 1) / span;
+    const int g = grid_for(n_spans);
     if (plan->dtype == ZERO_BF16)
-        adam_kernel<ZERO_BF16><<<g, kBlock, 0, s>>>(plan->dev, A);
+        adam_kernel<ZERO_BF16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
     else
-        adam_kernel<ZERO_FP16><<<g, kBlock, 0, s>>>(plan->dev, A);
+        adam_kernel<ZERO_FP16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
     return check_launch("zero_adam_step");
 }

@@ -20,92 +20,207 @@
 namespace zs {
 
 // ------------------------------------------------------------------------------- pack --
-// Block w of the grid-stride loop handles tile (w mod n_tile) of row (w / n_tile) of the
-// bucket; one thread per 8-column chunk.
-__global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t tile0,
-                                                      int64_t n_tile, const uint16_t* const* __restrict__ grads,
-                                                      uint16_t* __restrict__ packed) {
-    const int64_t n_work = n_tile * P.nd;
-    for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        const int64_t k = w / n_tile;
-        const int64_t j = tile0 + (w - k * n_tile);
-        const int64_t x = (j << kTileShift) + int64_t(threadIdx.x) * kChunk;  // shard column
-        if (x < b_base || x >= b_base + b_stride) continue;
-        uint16_t* dst = packed + k * b_stride + (x - b_base);
-        int64_t i = param_of_column(P, x);
-        if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) {
-            // Chunk inside parameter i.
-            const uint16_t* g = grads[i];
-            if (!g) continue;  // no gradient this step: leave the slots alone
-            const int64_t numel = P.numel[i];
-            const int64_t e0 = k * P.s[i] + (x - P.off[i]);
-            uint4 v;
-            if (e0 + kChunk <= numel && aligned16(g)) {
-                v = load8_realigned(g, e0);
-            } else {
-                uint16_t h[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? g[e0 + t] : uint16_t(0);
-                v = pack8(h);
-            }
-            *reinterpret_cast<uint4*>(dst) = v;
+#ifndef ZS_PACK_ROWS
+#define ZS_PACK_ROWS 1
+#endif
+#ifndef ZS_PACK_TILE_FASTEST
+#define ZS_PACK_TILE_FASTEST 0
+#endif
+#ifndef ZS_UNPACK_UNROLL
+#define ZS_UNPACK_UNROLL 1
+#endif
+constexpr int kPackRows = ZS_PACK_ROWS;          // rows per block iteration of the pack
+constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
+
+// Generic per-thread pack of one 8-column chunk of row k (parameter boundaries, padding,
+// row gaps, dead parameters, unaligned sources).  i is the first parameter with end > x.
+__device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, int64_t k, int64_t x,
+                                                   const uint16_t* const* __restrict__ grads, uint16_t* dst) {
+    if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) {
+        const uint16_t* g = grads[i];
+        if (!g) return;  // no gradient this step: leave the slots alone
+        const int64_t numel = P.numel[i];
+        const int64_t e0 = k * P.s[i] + (x - P.off[i]);
+        uint4 v;
+        if (e0 + kChunk <= numel && aligned16(g)) {
+            v = load8_realigned(g, e0);
         } else {
-            // Chunk across parameter boundaries, padding or the row gap: element by element.
+            const ZS_GLOBAL uint16_t* gg = gptr(g);
             uint16_t h[8];
-            unsigned keep = 0;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int64_t xt = x + t;
-                while (i < P.n && P.end[i] <= xt) ++i;
-                h[t] = 0;
-                if (i < P.n && P.off[i] <= xt) {
-                    const uint16_t* g = grads[i];
-                    if (!g) continue;
-                    const int64_t e = k * P.s[i] + (xt - P.off[i]);
-                    if (e < P.numel[i]) h[t] = g[e];
-                }
-                keep |= 1u << t;
-            }
-            if (keep == 0xffu) {
-                *reinterpret_cast<uint4*>(dst) = pack8(h);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 8; ++t)
-                    if (keep & (1u << t)) dst[t] = h[t];
-            }
+            for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
+            v = pack8(h);
         }
+        store16(dst, v);
+        return;
+    }
+    uint16_t h[8];
+    unsigned keep = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int64_t xt = x + t;
+        while (i < P.n && P.end[i] <= xt) ++i;
+        h[t] = 0;
+        if (i < P.n && P.off[i] <= xt) {
+            const uint16_t* g = grads[i];
+            if (!g) continue;
+            const int64_t e = k * P.s[i] + (xt - P.off[i]);
+            if (e < P.numel[i]) h[t] = gptr(g)[e];
+        }
+        keep |= 1u << t;
+    }
+    if (keep == 0xffu) {
+        store16(dst, pack8(h));
+    } else {
+        ZS_GLOBAL uint16_t* d = gptr(dst);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            if (keep & (1u << t)) d[t] = h[t];
+    }
+}
+
+// Work item w = (tile, group of kPackRows rows) of the bucket, rows varying fastest.  When
+// the whole tile lies inside one parameter with a 16-byte aligned gradient (decided once per
+// block from scalar loads), each thread issues the loads of all its rows before any store.
+__global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t tile0,
+                                                      int64_t n_tile, int64_t n_rg,
+                                                      const uint16_t* const* __restrict__ grads,
+                                                      uint16_t* __restrict__ packed) {
+    const int64_t n_work = n_tile * n_rg;
+    for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
+#if ZS_PACK_TILE_FASTEST
+        const int64_t rg = w / n_tile;
+        const int64_t jt = w - rg * n_tile;
+        const int64_t k0 = rg * kPackRows;
+#else
+        const int64_t jt = w / n_rg;
+        const int64_t k0 = (w - jt * n_rg) * kPackRows;
+#endif
+        const int64_t kend = k0 + kPackRows < P.nd ? k0 + kPackRows : P.nd;
+        const int64_t j = tile0 + jt;
+        const int64_t x0 = j << kTileShift;
+        const int64_t x = x0 + int64_t(threadIdx.x) * kChunk;
+        // The tile's parameter fields, read once per block (scalar loads; index clamped into
+        // range): the dependent chain is tile map -> fields and pointer -> data.
+        const int64_t iu = ld_const(P.tile_first, j);
+        const int64_t ic = iu < P.n ? iu : P.n - 1;
+        const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
+        const int64_t s = ld_const(P.s, ic), numel = ld_const(P.numel, ic);
+        const uint16_t* g = ld_const(grads, ic);
+        const bool whole = iu < P.n && off <= x0 && end >= x0 + kTileCols;
+        if (whole && !g) continue;  // the whole tile belongs to a parameter without a gradient
+        if (whole && aligned16(g)) {
+            const int64_t c = x - off;
+            const bool direct = ((s | off) & 7) == 0;  // every source chunk 16-byte aligned
+            uint16_t* dst = packed + (x - b_base);
+            uint4 v[kPackRows];
+#pragma unroll
+            for (int u = 0; u < kPackRows; ++u) {
+                const int64_t k = k0 + u;
+                if (k >= kend) break;
+                const int64_t e0 = k * s + c;
+                if (e0 + kChunk <= numel) {
+                    v[u] = direct ? load16(g + e0) : load8_realigned(g, e0);
+                } else {
+                    const ZS_GLOBAL uint16_t* gg = gptr(g);
+                    uint16_t h[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
+                    v[u] = pack8(h);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kPackRows; ++u) {
+                const int64_t k = k0 + u;
+                if (k >= kend) break;
+                store16(dst + k * b_stride, v[u]);
+            }
+            continue;
+        }
+        if (x < b_base || x >= b_base + b_stride) continue;
+        const int64_t i = param_of_column(P, x);
+        for (int64_t k = k0; k < kend; ++k) pack_chunk_generic(P, i, k, x, grads, packed + k * b_stride + (x - b_base));
     }
 }
 
 // ----------------------------------------------------------------------------- unpack --
-// One thread per 8-element chunk of a parameter's flat; chunks of the bucket's parameters
-// are numbered [u0, u1) in the plan's chunk space.
+// Generic per-thread unpack of chunk u (parameter boundaries, row crossings, tails,
+// unaligned outputs).
+__device__ __forceinline__ void unpack_chunk_generic(const DevPlan& P, int64_t u, int64_t b_base, int64_t b_stride,
+                                                     const uint16_t* __restrict__ gathered,
+                                                     uint16_t* const* __restrict__ outs) {
+    const int64_t i = param_of_chunk(P, u);
+    uint16_t* out = outs[i];
+    if (!out) return;
+    const int64_t numel = P.numel[i], s = P.s[i];
+    const int64_t col = P.off[i] - b_base;
+    const int64_t e0 = (u - P.ucb[i]) * kChunk;
+    // row k = e0 / s and column j0 = e0 mod s; the double estimate is off by at most one
+    int64_t k = int64_t(double(e0) * P.inv_s[i]);
+    int64_t j0 = e0 - k * s;
+    if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
+    if (e0 + kChunk <= numel && j0 + kChunk <= s && aligned16(out)) {
+        store16(out + e0, load8_realigned(gathered, k * b_stride + col + j0));
+    } else {
+        const int cnt = int(numel - e0 < kChunk ? numel - e0 : kChunk);
+        ZS_GLOBAL uint16_t* o = gptr(out);
+        const ZS_GLOBAL uint16_t* gsrc = gptr(gathered);
+        for (int t = 0; t < cnt; ++t) {
+            o[e0 + t] = gsrc[k * b_stride + col + j0];
+            if (++j0 == s) { j0 = 0; ++k; }
+        }
+    }
+}
+
+// One block iteration covers kUnpackUnroll consecutive chunk tiles (256 chunks each); a
+// thread takes one chunk of each.  Chunks of the bucket's parameters are [u0, u1).
 __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t u0,
                                                         int64_t u1, const uint16_t* __restrict__ gathered,
                                                         uint16_t* const* __restrict__ outs) {
     const int64_t ut0 = u0 >> kUTileShift;
-    const int64_t n_tiles = ((u1 + kUTileChunks - 1) >> kUTileShift) - ut0;
-    for (int64_t w = blockIdx.x; w < n_tiles; w += gridDim.x) {
-        const int64_t u = ((ut0 + w) << kUTileShift) + threadIdx.x;
-        if (u < u0 || u >= u1) continue;
-        const int64_t i = param_of_chunk(P, u);
-        uint16_t* out = outs[i];
-        if (!out) continue;
-        const int64_t numel = P.numel[i], s = P.s[i];
-        const int64_t col = P.off[i] - b_base;
-        const int64_t e0 = (u - P.ucb[i]) * kChunk;
-        // row k = e0 / s and column j0 = e0 mod s; the double estimate is off by at most one
-        int64_t k = int64_t(double(e0) * P.inv_s[i]);
-        int64_t j0 = e0 - k * s;
-        if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
-        if (e0 + kChunk <= numel && j0 + kChunk <= s && aligned16(out)) {
-            *reinterpret_cast<uint4*>(out + e0) = load8_realigned(gathered, k * b_stride + col + j0);
-        } else {
-            const int cnt = int(numel - e0 < kChunk ? numel - e0 : kChunk);
-            for (int t = 0; t < cnt; ++t) {
-                out[e0 + t] = gathered[k * b_stride + col + j0];
-                if (++j0 == s) { j0 = 0; ++k; }
+    const int64_t n_ut = ((u1 + kUTileChunks - 1) >> kUTileShift) - ut0;
+    const int64_t n_groups = (n_ut + kUnpackUnroll - 1) / kUnpackUnroll;
+    for (int64_t w = blockIdx.x; w < n_groups; w += gridDim.x) {
+        const int64_t ut = ut0 + w * kUnpackUnroll;
+        const int64_t ua = ut << kUTileShift;
+        const int64_t ub = ua + kUnpackUnroll * kUTileChunks;
+        // parameter fields read once per block (scalar loads; index clamped into range)
+        const int64_t iu = ld_const(P.utile_first, ut);
+        const int64_t ic = iu < P.n ? iu : P.n - 1;
+        const int64_t ucb = ld_const(P.ucb, ic), ucend = ld_const(P.ucend, ic);
+        const int64_t numel = ld_const(P.numel, ic), s = ld_const(P.s, ic);
+        const int64_t col = ld_const(P.off, ic) - b_base;
+        const double inv_s = ld_const(P.inv_s, ic);
+        uint16_t* const out = ld_const(outs, ic);
+        const bool whole = ua >= u0 && ub <= u1 && iu < P.n && ucb <= ua && ucend >= ub;
+        if (whole && !out) continue;  // every chunk of the group belongs to a skipped parameter
+        if (whole && aligned16(out)) {
+            // every chunk of the group belongs to parameter iu
+            uint4 v[kUnpackUnroll];
+            int64_t e[kUnpackUnroll];
+            bool ok[kUnpackUnroll];
+#pragma unroll
+            for (int t = 0; t < kUnpackUnroll; ++t) {
+                const int64_t u = ua + t * kUTileChunks + threadIdx.x;
+                const int64_t e0 = (u - ucb) * kChunk;
+                int64_t k = int64_t(double(e0) * inv_s);
+                int64_t j0 = e0 - k * s;
+                if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
+                e[t] = e0;
+                ok[t] = e0 + kChunk <= numel && j0 + kChunk <= s;
+                if (ok[t]) v[t] = load8_realigned(gathered, k * b_stride + col + j0);
             }
+#pragma unroll
+            for (int t = 0; t < kUnpackUnroll; ++t) {
+                if (ok[t]) store16(out + e[t], v[t]);
+                else unpack_chunk_generic(P, ua + t * kUTileChunks + threadIdx.x, b_base, b_stride, gathered, outs);
+            }
+            continue;
+        }
+#pragma unroll
+        for (int t = 0; t < kUnpackUnroll; ++t) {
+            const int64_t u = ua + t * kUTileChunks + threadIdx.x;
+            if (u >= u0 && u < u1) unpack_chunk_generic(P, u, b_base, b_stride, gathered, outs);
         }
     }
 }
@@ -131,20 +246,20 @@ __global__ __launch_bounds__(kBlock) void shard_init_kernel(DevPlan P, const voi
                 if (!src) continue;
                 const int64_t e = P.rank * P.s[i] + (xt - P.off[i]);
                 if (e < P.numel[i]) {
-                    if constexpr (SRC == 0) vals[t] = static_cast<const float*>(src)[e];
-                    else vals[t] = to_f32<SRC>(static_cast<const uint16_t*>(src)[e]);
+                    if constexpr (SRC == 0) vals[t] = gptr(static_cast<const float*>(src))[e];
+                    else vals[t] = to_f32<SRC>(gptr(static_cast<const uint16_t*>(src))[e]);
                 }
             }
             keep |= 1u << t;
         }
         float* dst = p32 + x;
         if (keep == 0xffu) {
-            reinterpret_cast<float4*>(dst)[0] = make_float4(vals[0], vals[1], vals[2], vals[3]);
-            reinterpret_cast<float4*>(dst)[1] = make_float4(vals[4], vals[5], vals[6], vals[7]);
+            store4f(dst, make_float4(vals[0], vals[1], vals[2], vals[3]));
+            store4f(dst + 4, make_float4(vals[4], vals[5], vals[6], vals[7]));
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                if (keep & (1u << t)) dst[t] = vals[t];
+                if (keep & (1u << t)) gptr(dst)[t] = vals[t];
         }
     }
 }
@@ -167,8 +282,9 @@ extern "C" zero_status zero_pack_bucket(const zero_plan* plan, int64_t b, const 
     if (stride == 0) return ZERO_OK;
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + stride + kTileCols - 1) >> kTileShift) - tile0;
-    pack_kernel<<<grid_for(n_tile * plan->nd, 8192), kBlock, 0, (hipStream_t)stream>>>(
-        plan->dev, base, stride, tile0, n_tile, reinterpret_cast<const uint16_t* const*>(d_grad_ptrs),
+    const int64_t n_rg = (plan->nd + kPackRows - 1) / kPackRows;
+    pack_kernel<<<grid_for(n_tile * n_rg), kBlock, 0, (hipStream_t)stream>>>(
+        plan->dev, base, stride, tile0, n_tile, n_rg, reinterpret_cast<const uint16_t* const*>(d_grad_ptrs),
         static_cast<uint16_t*>(d_packed));
     return check_launch("zero_pack_bucket");
 }
@@ -183,8 +299,8 @@ extern "C" zero_status zero_unpack(const zero_plan* plan, int64_t b, const void*
     const int64_t* br = bucket_row(plan, b);
     const int64_t u0 = plan->h_bucket_chunks[2 * b], u1 = plan->h_bucket_chunks[2 * b + 1];
     if (u1 == u0) return ZERO_OK;
-    const int64_t n_tiles = ((u1 + kUTileChunks - 1) >> kUTileShift) - (u0 >> kUTileShift);
-    unpack_kernel<<<grid_for(n_tiles, 8192), kBlock, 0, (hipStream_t)stream>>>(
+    const int64_t n_ut = ((u1 + kUTileChunks - 1) >> kUTileShift) - (u0 >> kUTileShift);
+    unpack_kernel<<<grid_for((n_ut + kUnpackUnroll - 1) / kUnpackUnroll), kBlock, 0, (hipStream_t)stream>>>(
         plan->dev, br[BF_BASE], br[BF_STRIDE], u0, u1, static_cast<const uint16_t*>(d_gathered),
         reinterpret_cast<uint16_t* const*>(d_param_ptrs));
     return check_launch("zero_unpack");
@@ -197,7 +313,7 @@ extern "C" zero_status zero_shard_init(const zero_plan* plan, const void* const*
     if (!d_src_ptrs || !d_p32) return fail(ZERO_EINVAL, "zero_shard_init: NULL pointer");
     if (!host_aligned16(d_p32)) return fail(ZERO_EINVAL, "zero_shard_init: p32 not 16-byte aligned");
     if (plan->shard_numel == 0) return ZERO_OK;
-    const int g = grid_for(plan->dev.n_tiles, 8192);
+    const int g = grid_for(plan->dev.n_tiles);
     hipStream_t s = (hipStream_t)stream;
     switch (src_dtype) {
         case 0: shard_init_kernel<0><<<g, kBlock, 0, s>>>(plan->dev, d_src_ptrs, d_p32); break;

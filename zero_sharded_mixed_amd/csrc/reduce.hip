@@ -43,31 +43,41 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_bas
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
     const int64_t nd = P.nd;
     for (int64_t w = blockIdx.x; w < n_tile; w += gridDim.x) {
-        const int64_t x = ((tile0 + w) << kTileShift) + int64_t(threadIdx.x) * kChunk;
+        const int64_t j = tile0 + w;
+        const int64_t x0 = j << kTileShift;
+        // block-uniform (scalar loads): does the whole tile lie inside one parameter, hence
+        // inside this bucket, and is that parameter live?
+        const int64_t iu = ld_const(P.tile_first, j);
+        const int64_t ic = iu < P.n ? iu : P.n - 1;
+        const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
+        const bool lv = ld_const(live, ic) != 0;
+        const bool whole = iu < P.n && off <= x0 && end >= x0 + kTileCols;
+        if (whole && !lv) continue;
+        const int64_t x = x0 + int64_t(threadIdx.x) * kChunk;
         const int64_t c = x - b_base;
-        if (c < 0 || c >= b_row) continue;  // outside the bucket, or entirely in the row gap
-        const unsigned mask = live_mask8(P, live, x, param_of_column(P, x));
+        if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
+        const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
         if (mask == 0) continue;
         const uint16_t* src = rows + c;
         float acc[8];
-        accumulate8<DT, true>(acc, *reinterpret_cast<const uint4*>(src));
+        accumulate8<DT, true>(acc, load16(src));
         int64_t k = 1;
         for (; k + kAhead <= nd; k += kAhead) {
             uint4 v[kAhead];
 #pragma unroll
-            for (int u = 0; u < kAhead; ++u) v[u] = *reinterpret_cast<const uint4*>(src + (k + u) * row_stride);
+            for (int u = 0; u < kAhead; ++u) v[u] = load16(src + (k + u) * row_stride);
 #pragma unroll
             for (int u = 0; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
         }
-        for (; k < nd; ++k) accumulate8<DT, false>(acc, *reinterpret_cast<const uint4*>(src + k * row_stride));
+        for (; k < nd; ++k) accumulate8<DT, false>(acc, load16(src + k * row_stride));
         float* dst = g32 + x;
         if (mask == 0xffu) {
-            reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+            store4f(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
+            store4f(dst + 4, make_float4(acc[4], acc[5], acc[6], acc[7]));
         } else {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                if (mask & (1u << t)) dst[t] = acc[t];
+                if (mask & (1u << t)) gptr(dst)[t] = acc[t];
         }
         if (flag) flag_if_bad(acc, mask, flag);
     }
@@ -80,8 +90,8 @@ __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float
         if (x >= P.shard_numel) continue;
         const unsigned mask = live_mask8(P, live, x, param_of_column(P, x));
         if (mask == 0) continue;
-        const float4 a = reinterpret_cast<const float4*>(g32 + x)[0];
-        const float4 b = reinterpret_cast<const float4*>(g32 + x)[1];
+        const float4 a = load4f(g32 + x);
+        const float4 b = load4f(g32 + x + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         flag_if_bad(v, mask, flag);
     }
@@ -107,7 +117,7 @@ extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const
     if (row == 0) return ZERO_OK;
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
-    const int g = grid_for(n_tile, 8192);
+    const int g = grid_for(n_tile);
     hipStream_t s = (hipStream_t)stream;
     const uint16_t* rows = static_cast<const uint16_t*>(d_rows);
     if (plan->dtype == ZERO_BF16)
@@ -126,7 +136,7 @@ extern "C" zero_status zero_overflow_check(const zero_plan* plan, const float* d
     if (!d_g32 || !d_live || !d_flag) return fail(ZERO_EINVAL, "zero_overflow_check: NULL pointer");
     if (!host_aligned16(d_g32)) return fail(ZERO_EINVAL, "zero_overflow_check: g32 not 16-byte aligned");
     if (plan->shard_numel == 0) return ZERO_OK;
-    overflow_kernel<<<grid_for(plan->dev.n_tiles, 8192), kBlock, 0, (hipStream_t)stream>>>(plan->dev, d_g32, d_live,
+    overflow_kernel<<<grid_for(plan->dev.n_tiles), kBlock, 0, (hipStream_t)stream>>>(plan->dev, d_g32, d_live,
                                                                                           d_flag);
     return check_launch("zero_overflow_check");
 }

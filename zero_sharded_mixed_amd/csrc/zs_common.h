@@ -50,6 +50,29 @@ struct DevPlan {
     const int32_t* utile_first;  // [n_utiles + 1]
 };
 
+// Address-space helpers.  Plan tables are never written by the hot kernels: reading them
+// through the constant address space lets a block-uniform index become a scalar load.  Data
+// pointers taken from the caller's pointer tables are generic; casting them to the global
+// address space gives global (not flat) loads and stores.
+#define ZS_CONST __attribute__((address_space(4)))
+#define ZS_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+    return ((const ZS_CONST T*)p)[i];
+}
+__device__ __forceinline__ float2 ld_const_f2(const float2* p, int64_t i) {
+    const uint64_t u = ld_const(reinterpret_cast<const uint64_t*>(p), i);
+    return make_float2(__uint_as_float(uint32_t(u)), __uint_as_float(uint32_t(u >> 32)));
+}
+template <class T>
+__device__ __forceinline__ const ZS_GLOBAL T* gptr(const T* p) {
+    return (const ZS_GLOBAL T*)p;
+}
+template <class T>
+__device__ __forceinline__ ZS_GLOBAL T* gptr(T* p) {
+    return (ZS_GLOBAL T*)p;
+}
+
 // First index i in [lo, hi] with key[i] > x, given key non-decreasing and key[hi] > x
 // (or hi == n).  Returns hi when none before it qualifies.
 __device__ __forceinline__ int64_t first_greater(const int64_t* __restrict__ key, int64_t lo, int64_t hi, int64_t x) {
@@ -64,41 +87,58 @@ __device__ __forceinline__ int64_t first_greater(const int64_t* __restrict__ key
 // The caller checks off_i <= x (otherwise x lies in a row gap).
 __device__ __forceinline__ int64_t param_of_column(const DevPlan& P, int64_t x) {
     int64_t j = x >> kTileShift;
-    return first_greater(P.end, P.tile_first[j], P.tile_first[j + 1], x);
+    return first_greater(P.end, ld_const(P.tile_first, j), ld_const(P.tile_first, j + 1), x);
 }
 
 // Parameter owning unpack chunk u (first i with ucend_i > u).
 __device__ __forceinline__ int64_t param_of_chunk(const DevPlan& P, int64_t u) {
     int64_t j = u >> kUTileShift;
-    return first_greater(P.ucend, P.utile_first[j], P.utile_first[j + 1], u);
+    return first_greater(P.ucend, ld_const(P.utile_first, j), ld_const(P.utile_first, j + 1), u);
+}
+
+// 16-byte global loads and stores (native vector types: the HIP vector classes cannot be
+// copied across address spaces).
+typedef uint32_t zs_u32x4 __attribute__((ext_vector_type(4)));
+typedef float zs_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16(const void* p) {
+    const zs_u32x4 w = *gptr(reinterpret_cast<const zs_u32x4*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ void store16(void* p, const uint4& v) {
+    zs_u32x4 w = {v.x, v.y, v.z, v.w};
+    *gptr(reinterpret_cast<zs_u32x4*>(p)) = w;
+}
+__device__ __forceinline__ float4 load4f(const float* p) {
+    const zs_f32x4 w = *gptr(reinterpret_cast<const zs_f32x4*>(p));
+    return make_float4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ void store4f(float* p, const float4& v) {
+    zs_f32x4 w = {v.x, v.y, v.z, v.w};
+    *gptr(reinterpret_cast<zs_f32x4*>(p)) = w;
 }
 
 // Eight consecutive 16-bit elements starting at element e of a 16-byte aligned buffer,
-// assembled from the aligned 16-byte granules that hold them.  Never touches a granule that
-// holds none of the eight elements.
+// assembled from the aligned 16-byte granules that hold them (never a granule that holds
+// none of the eight).  Branch-free: the d = e mod 8 element shift is a selection of 32-bit
+// words by d/2 followed by a 2-byte funnel shift when d is odd.
 __device__ __forceinline__ uint4 load8_realigned(const uint16_t* __restrict__ base, int64_t e) {
-    const uint4* v = reinterpret_cast<const uint4*>(base);
     const int64_t q = e >> 3;
     const int d = int(e & 7);
-    const uint4 a = v[q];
+    const uint4 a = load16(base + 8 * q);
     if (d == 0) return a;
-    const uint4 b = v[q + 1];
+    const uint4 b = load16(base + 8 * q + 8);
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint4 r;
-    switch (d) {  // word shift by d/2, then a 2-byte shift when d is odd
-        case 1: r = make_uint4(__builtin_amdgcn_alignbyte(w[1], w[0], 2), __builtin_amdgcn_alignbyte(w[2], w[1], 2),
-                               __builtin_amdgcn_alignbyte(w[3], w[2], 2), __builtin_amdgcn_alignbyte(w[4], w[3], 2)); break;
-        case 2: r = make_uint4(w[1], w[2], w[3], w[4]); break;
-        case 3: r = make_uint4(__builtin_amdgcn_alignbyte(w[2], w[1], 2), __builtin_amdgcn_alignbyte(w[3], w[2], 2),
-                               __builtin_amdgcn_alignbyte(w[4], w[3], 2), __builtin_amdgcn_alignbyte(w[5], w[4], 2)); break;
-        case 4: r = make_uint4(w[2], w[3], w[4], w[5]); break;
-        case 5: r = make_uint4(__builtin_amdgcn_alignbyte(w[3], w[2], 2), __builtin_amdgcn_alignbyte(w[4], w[3], 2),
-                               __builtin_amdgcn_alignbyte(w[5], w[4], 2), __builtin_amdgcn_alignbyte(w[6], w[5], 2)); break;
-        case 6: r = make_uint4(w[3], w[4], w[5], w[6]); break;
-        default: r = make_uint4(__builtin_amdgcn_alignbyte(w[4], w[3], 2), __builtin_amdgcn_alignbyte(w[5], w[4], 2),
-                                __builtin_amdgcn_alignbyte(w[6], w[5], 2), __builtin_amdgcn_alignbyte(w[7], w[6], 2)); break;
+    const int h = d >> 1;
+    const uint32_t sh = (d & 1) ? 2u : 0u;
+    uint32_t lo[5];
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {  // lo[t] = w[h + t] (h in 0..3, h + t <= 7)
+        const uint32_t c0 = w[t], c1 = w[t + 1 < 8 ? t + 1 : 7], c2 = w[t + 2 < 8 ? t + 2 : 7],
+                       c3 = w[t + 3 < 8 ? t + 3 : 7];
+        lo[t] = h == 0 ? c0 : h == 1 ? c1 : h == 2 ? c2 : c3;
     }
-    return r;
+    return make_uint4(__builtin_amdgcn_alignbyte(lo[1], lo[0], sh), __builtin_amdgcn_alignbyte(lo[2], lo[1], sh),
+                      __builtin_amdgcn_alignbyte(lo[3], lo[2], sh), __builtin_amdgcn_alignbyte(lo[4], lo[3], sh));
 }
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -184,7 +224,13 @@ zero_status fail(zero_status st, const char* fmt, ...);
 zero_status check_launch(const char* what);
 zero_status check_device(const zero_plan* plan);
 inline bool host_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-inline int grid_for(int64_t work, int64_t cap = 4096) {
+// Hot kernels launch one block per work item (a tile, or a tile of one row): on MI355X a
+// one-shot grid with one 16-byte chunk per thread streams faster than a grid-stride loop.  The
+// kernels still loop, so any grid size is correct.
+#ifndef ZS_GRID_CAP
+#define ZS_GRID_CAP (int64_t(1) << 30)
+#endif
+inline int grid_for(int64_t work, int64_t cap = ZS_GRID_CAP) {
     return int(work < 1 ? 1 : (work < cap ? work : cap));
 }
 }  // namespace zs
