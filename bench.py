@@ -162,7 +162,9 @@ def run_gpu(w, steps, warmup, device):
         for j, p in enumerate(phases):
             per_phase[p] += ev[j].elapsed_time(ev[j + 1])
     per_phase = {p: v / steps for p, v in per_phase.items()}  # ms per step
-    launches = {"pack": len(st.buckets), "reduce": len(st.buckets), "adam": 2, "unpack": len(st.buckets)}
+    # launches of each stage's streaming kernel (Adam's phase also holds its small per-parameter
+    # prepare kernel, a few microseconds)
+    launches = {"pack": len(st.buckets), "reduce": len(st.buckets), "adam": 1, "unpack": len(st.buckets)}
     shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
     flag = int(st.flag.item())
     return wall / steps * 1e3, per_phase, launches, shard_sizes, flag
@@ -244,6 +246,93 @@ def cpu_baseline(w, max_elems: int):
                       f"single thread, plain C oracle"}
 
 
+# ------------------------------------------------------------------- profile summaries --
+
+KERNEL_KEYS = (("adam_prepare_kernel", "adam_prepare"), ("unpack_kernel", "unpack"), ("pack_kernel", "pack"),
+               ("reduce_kernel", "reduce"), ("adam_kernel", "adam"), ("overflow_kernel", "overflow"),
+               ("shard_init_kernel", "shard_init"))
+
+
+def _short(name: str) -> str:
+    for key, short in KERNEL_KEYS:
+        if key in name:
+            return short
+    return name[:60]
+
+
+def summarize_profiles(root: str, workload: str, command: str) -> str:
+    """Reduce rocprofv3 CSV output (root/trace: --kernel-trace --stats; root/FETCH_SIZE and
+    root/WRITE_SIZE: one --pmc pass each) to a short text summary, and record the HBM bytes
+    per launch of every pipeline kernel in profiles/traffic.json.  The counters are scaled by
+    what they read for torch's 2 GiB device copy (2 GiB fetched, 2 GiB written)."""
+    import csv
+    import glob
+
+    def rows(pattern):
+        files = glob.glob(os.path.join(root, pattern), recursive=True)
+        if not files:
+            raise FileNotFoundError(pattern)
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    lines = [f"# rocprofv3 summary — {workload}", "", "Commands (repo root as working directory):", "",
+             "```", command, "```", "", "## Kernel time (--kernel-trace --stats)", "",
+             "| kernel | calls | avg us | min us | max us | total ms | % |", "|---|---|---|---|---|---|---|"]
+    stats = rows("trace/**/*kernel_stats.csv")
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = _short(r["Name"])
+        if name not in dict(KERNEL_KEYS).values() and float(r["Percentage"]) < 1.0:
+            continue
+        lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    traffic = {}
+    counters = {}
+    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+        per = {}
+        for r in rows(f"{cname}/**/*counter_collection.csv"):
+            if r.get("Counter_Name", cname) != cname:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        counters[cname] = per
+    # calibration: the largest "copy" dispatches (torch's 2 GiB device copy)
+    copies = [(max(v), k) for k, v in counters["FETCH_SIZE"].items() if "copy" in k.lower()]
+    cal_kernel = max(copies)[1]
+    known_kib = 2.0 * 1024 * 1024
+    fetch_cal = max(counters["FETCH_SIZE"][cal_kernel])
+    write_cal = max(counters["WRITE_SIZE"].get(cal_kernel, [known_kib]))
+    f_fac, w_fac = known_kib / fetch_cal, known_kib / write_cal
+    lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", "",
+              f"Calibration: torch's 2 GiB device copy reads FETCH_SIZE {fetch_cal:.0f} KiB and WRITE_SIZE "
+              f"{write_cal:.0f} KiB against 2097152 KiB each: factors {f_fac:.4f} (fetch), {w_fac:.4f} (write).", "",
+              "| kernel | dispatches | avg FETCH KiB | avg WRITE KiB | scaled bytes / dispatch |", "|---|---|---|---|---|"]
+    src_hash = kernel_source_hash()
+    for kname, vals in counters["FETCH_SIZE"].items():
+        short = _short(kname)
+        if short not in dict(KERNEL_KEYS).values():
+            continue
+        wv = counters["WRITE_SIZE"].get(kname, [0.0])
+        fk, wk = sum(vals) / len(vals), sum(wv) / len(wv)
+        b = fk * 1024 * f_fac + wk * 1024 * w_fac
+        prev = traffic.get(short)
+        if prev:  # several instantiations (dtypes) of one kernel: keep the busiest
+            if prev["bytes_per_launch"] >= b:
+                continue
+        traffic[short] = {"bytes_per_launch": int(b), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                          "dispatches": len(vals), "source_hash": src_hash}
+        lines.append(f"| {short} | {len(vals)} | {fk:.0f} | {wk:.0f} | {b:.3e} |")
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            allt = json.load(fh)
+    except (OSError, ValueError):
+        allt = {}
+    allt[workload] = traffic
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allt, fh, indent=1, sort_keys=True)
+    return "\n".join(lines) + "\n"
+
+
 # -------------------------------------------------------------------------------- main --
 
 def main():
@@ -255,7 +344,14 @@ def main():
     ap.add_argument("--cpu-sample-elems", type=int, default=800_000_000,
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="reduce rocprofv3 CSVs under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/) to a text summary "
+                         "on stdout and profiles/traffic.json, then exit")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        print(summarize_profiles(args.summarize_profiles, "gpt2-1.5b-nd8-r0", args.profile_command), end="")
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU reduce-scatter/all-gather path is not built)", file=sys.stderr)
