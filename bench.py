@@ -341,7 +341,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload: 2 = GPT-2 1.5B-shaped list (default)")
-    ap.add_argument("--cpu-sample-elems", type=int, default=800_000_000,
+    ap.add_argument("--cpu-sample-elems", type=int, default=1_600_000_000,
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-profiles", metavar="DIR",

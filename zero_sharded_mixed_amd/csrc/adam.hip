@@ -63,13 +63,21 @@ struct AdamK {
     float b1, b2, c1, c2, eps, gs;
 };
 
+#ifndef ZS_ADAM_FAST_MATH
+#define ZS_ADAM_FAST_MATH 0
+#endif
 __device__ __forceinline__ void adam_elem(const AdamK& K, float g32, float& p, float& m, float& v, float step_size,
                                           float inv_sqrt_bc2) {
     const float g = g32 * K.gs;
     m = K.b1 * m + K.c1 * g;
     v = K.b2 * v + K.c2 * (g * g);
+#if ZS_ADAM_FAST_MATH
+    const float denom = __builtin_amdgcn_sqrtf(v) * inv_sqrt_bc2 + K.eps;
+    p = p - step_size * (m * __builtin_amdgcn_rcpf(denom));
+#else
     const float denom = sqrtf(v) * inv_sqrt_bc2 + K.eps;
     p = p - step_size * (m / denom);
+#endif
 }
 
 #ifndef ZS_ADAM_COLS

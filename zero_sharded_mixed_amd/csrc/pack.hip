@@ -21,10 +21,7 @@ namespace zs {
 
 // ------------------------------------------------------------------------------- pack --
 #ifndef ZS_PACK_ROWS
-#define ZS_PACK_ROWS 1
-#endif
-#ifndef ZS_PACK_TILE_FASTEST
-#define ZS_PACK_TILE_FASTEST 0
+#define ZS_PACK_ROWS 2
 #endif
 #ifndef ZS_UNPACK_UNROLL
 #define ZS_UNPACK_UNROLL 1
@@ -79,23 +76,20 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
     }
 }
 
-// Work item w = (tile, group of kPackRows rows) of the bucket, rows varying fastest.  When
-// the whole tile lies inside one parameter with a 16-byte aligned gradient (decided once per
-// block from scalar loads), each thread issues the loads of all its rows before any store.
+// Work item w = (tile, group of kPackRows rows) of the bucket, rows varying fastest (on MI355X
+// this dispatch order streams faster than tile-fastest).  When the whole tile lies inside one
+// parameter with a 16-byte aligned gradient (decided once per block from scalar loads), each
+// thread issues the loads of its rows before any store.
 __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t tile0,
                                                       int64_t n_tile, int64_t n_rg,
                                                       const uint16_t* const* __restrict__ grads,
                                                       uint16_t* __restrict__ packed) {
     const int64_t n_work = n_tile * n_rg;
     for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-#if ZS_PACK_TILE_FASTEST
-        const int64_t rg = w / n_tile;
-        const int64_t jt = w - rg * n_tile;
-        const int64_t k0 = rg * kPackRows;
-#else
-        const int64_t jt = w / n_rg;
+        int64_t jt;
+        if (n_work <= int64_t(UINT32_MAX)) jt = int64_t(uint32_t(w) / uint32_t(n_rg));  // 32-bit divide
+        else jt = w / n_rg;
         const int64_t k0 = (w - jt * n_rg) * kPackRows;
-#endif
         const int64_t kend = k0 + kPackRows < P.nd ? k0 + kPackRows : P.nd;
         const int64_t j = tile0 + jt;
         const int64_t x0 = j << kTileShift;

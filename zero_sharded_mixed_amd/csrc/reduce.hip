@@ -36,50 +36,66 @@ __device__ __forceinline__ void flag_if_bad(const float (&v)[8], unsigned mask, 
     if (bad) atomicOr(flag, 1);
 }
 
+#ifndef ZS_REDUCE_TILES
+#define ZS_REDUCE_TILES 1
+#endif
+constexpr int kReduceTiles = ZS_REDUCE_TILES;  // consecutive tiles per block (one chunk of each per thread)
+
+template <int DT>
+__device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, int64_t c, unsigned mask,
+                                             const uint16_t* __restrict__ rows, int64_t row_stride,
+                                             float* __restrict__ g32, int32_t* __restrict__ flag) {
+    const int64_t nd = P.nd;
+    const uint16_t* src = rows + c;
+    float acc[8];
+    accumulate8<DT, true>(acc, load16(src));
+    int64_t k = 1;
+    for (; k + kAhead <= nd; k += kAhead) {
+        uint4 v[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) v[u] = load16(src + (k + u) * row_stride);
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
+    }
+    for (; k < nd; ++k) accumulate8<DT, false>(acc, load16(src + k * row_stride));
+    float* dst = g32 + x;
+    if (mask == 0xffu) {
+        store4f(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
+        store4f(dst + 4, make_float4(acc[4], acc[5], acc[6], acc[7]));
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            if (mask & (1u << t)) gptr(dst)[t] = acc[t];
+    }
+    if (flag) flag_if_bad(acc, mask, flag);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_base, int64_t b_row, int64_t tile0,
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
-    const int64_t nd = P.nd;
-    for (int64_t w = blockIdx.x; w < n_tile; w += gridDim.x) {
-        const int64_t j = tile0 + w;
+    const int64_t n_groups = (n_tile + kReduceTiles - 1) / kReduceTiles;
+    for (int64_t w = blockIdx.x; w < n_groups; w += gridDim.x) {
+        const int64_t j = tile0 + w * kReduceTiles;
         const int64_t x0 = j << kTileShift;
-        // block-uniform (scalar loads): does the whole tile lie inside one parameter, hence
-        // inside this bucket, and is that parameter live?
+        // block-uniform (scalar loads): does the whole group of tiles lie inside one parameter,
+        // hence inside this bucket, and is that parameter live?
         const int64_t iu = ld_const(P.tile_first, j);
         const int64_t ic = iu < P.n ? iu : P.n - 1;
         const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
         const bool lv = ld_const(live, ic) != 0;
-        const bool whole = iu < P.n && off <= x0 && end >= x0 + kTileCols;
+        const bool whole = iu < P.n && off <= x0 && end >= x0 + kReduceTiles * kTileCols;
         if (whole && !lv) continue;
-        const int64_t x = x0 + int64_t(threadIdx.x) * kChunk;
-        const int64_t c = x - b_base;
-        if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
-        const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
-        if (mask == 0) continue;
-        const uint16_t* src = rows + c;
-        float acc[8];
-        accumulate8<DT, true>(acc, load16(src));
-        int64_t k = 1;
-        for (; k + kAhead <= nd; k += kAhead) {
-            uint4 v[kAhead];
 #pragma unroll
-            for (int u = 0; u < kAhead; ++u) v[u] = load16(src + (k + u) * row_stride);
-#pragma unroll
-            for (int u = 0; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
+        for (int t = 0; t < kReduceTiles; ++t) {
+            const int64_t x = x0 + t * kTileCols + int64_t(threadIdx.x) * kChunk;
+            const int64_t c = x - b_base;
+            if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
+            const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
+            if (mask == 0) continue;
+            reduce_chunk<DT>(P, x, c, mask, rows, row_stride, g32, flag);
         }
-        for (; k < nd; ++k) accumulate8<DT, false>(acc, load16(src + k * row_stride));
-        float* dst = g32 + x;
-        if (mask == 0xffu) {
-            store4f(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
-            store4f(dst + 4, make_float4(acc[4], acc[5], acc[6], acc[7]));
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                if (mask & (1u << t)) gptr(dst)[t] = acc[t];
-        }
-        if (flag) flag_if_bad(acc, mask, flag);
     }
 }
 
@@ -117,7 +133,7 @@ extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const
     if (row == 0) return ZERO_OK;
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
-    const int g = grid_for(n_tile);
+    const int g = grid_for((n_tile + kReduceTiles - 1) / kReduceTiles);
     hipStream_t s = (hipStream_t)stream;
     const uint16_t* rows = static_cast<const uint16_t*>(d_rows);
     if (plan->dtype == ZERO_BF16)
