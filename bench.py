@@ -32,6 +32,18 @@ import zero_sharded_mixed_amd as Z  # noqa: E402  (fails at first call if the HI
 HBM_PEAK_GBS = 8000.0
 METRIC = "shard step GB/s & elem/s (pack+reduce+Adam) vs HBM peak, 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+WORKLOAD_IDS = {2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63", 5: "ragged-10k-nd1024-r517"}
+WORKLOAD_TEXT = {
+    2: "GPT-2 1.5B-shaped parameter list (48 layers, d=1600, vocab 50257, 1024 positions); Nd=8 virtual ranks, "
+       "rank 0, 500M-element buckets; bf16 grads N(0,1e-3) and params, fp32 master N(0,0.02) / m / v; Adam lr 1e-3, "
+       "betas (0.9, 0.999), eps 1e-8",
+    3: "Llama-7B-shaped parameter list (32 layers, d=4096, ffn 11008, vocab 32000, untied head); Nd=8, rank 5, "
+       "500M-element buckets; bf16 grads N(0,1e-3) with 1% exact zeros; fp32 master / m / v",
+    4: "7.5B paper-style list (72 layers, d=2880, odd-sized biases forcing padding); Nd=64, rank 63; fp16 grads "
+       "N(0,1e-3) x 2^16 loss scale; fp32 master / m / v",
+    5: "ragged list of 10,000 parameters, numel log-uniform in [1, 4M]; Nd=1024, rank 517; 30% without gradient; "
+       "fp16 grads N(0,1e-2); fp32 master / m / v",
+}
 
 
 def log(*a):
@@ -123,10 +135,67 @@ def setup_gpu(w, device):
     return st, own, packed_all, rows_of, lp, lp_ptrs, live
 
 
+def setup_gpu_rows(w, device):
+    """Row-only emulation (lists whose Nd full gradient copies would not fit): the other
+    virtual ranks' rows r are generated directly per bucket, with the positions a packer leaves
+    zero (padding, dead parameters, the row gap) set to +0.  Row r is this rank's own packed
+    row, copied once: the gradients are the same in every timed step, so the reduce reads
+    exactly what the step's pack writes."""
+    import workloads as W
+
+    torch.cuda.set_device(device)
+    t0 = time.time()
+    st = Z.ShardStep(w.numels, w.nd, w.rank, w.bucket_bytes, w.dtype, device=device)
+    s = st.summary
+    log(f"[bench] plan: n={s.n_params} nd={s.nd} rank={s.rank} buckets={s.n_buckets} shard={s.shard_numel} "
+        f"psi={s.padded_total} ({time.time() - t0:.1f}s)")
+    masters = W.masters(w, device)
+    st.init_master(Z.ptr_table(masters), 0)
+    lp = [m.to(torch.bfloat16 if w.dtype == W.BF16 else torch.float16) for m in masters]
+    del masters
+    lp_ptrs = Z.ptr_table(lp)
+    st.pack(lp_ptrs, out=st.arena)
+    live = W.live_mask(w, 0)
+    st.live.copy_(torch.from_numpy(live))
+    g = W.grads(w, 0, w.rank, device)
+    gl = [t if l else None for t, l in zip(g, live)]
+    own_ptrs = Z.ptr_table(gl)
+    st.pack(own_ptrs)
+    info = [Z.zero_plan_param_info(st.plan, i) for i in range(st.n)]
+    recv = []
+    for b, bk in enumerate(st.buckets):
+        L = int(bk.row_stride)
+        keep = np.zeros(L, dtype=bool)
+        for i in range(int(bk.first_param), int(bk.first_param + bk.n_params)):
+            p = info[i]
+            if live[i]:
+                real = max(0, min(p.shard_size, p.numel - w.rank * p.shard_size))
+                keep[p.bucket_col:p.bucket_col + real] = True
+        zero = torch.from_numpy(~keep).to(device)
+        blk = torch.empty((w.nd, L), dtype=torch.int16, device=device)
+        for k in range(w.nd):
+            if k == w.rank:
+                blk[k].copy_(st.own_row(st.packed, b))
+            else:
+                blk[k].copy_(W.remote_row(w, 0, k, b, L, device).view(torch.int16))
+                blk[k].masked_fill_(zero, 0)
+        recv.append(blk)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB ({time.time() - t0:.1f}s)")
+
+    def rows_of(b):
+        return recv[b].view(-1), int(st.buckets[b].row_stride)
+
+    return st, (gl, own_ptrs), st.packed, rows_of, lp, lp_ptrs, live
+
+
 def run_gpu(w, steps, warmup, device):
-    st, own, packed_all, rows_of, lp, lp_ptrs, live = setup_gpu(w, device)
+    if w.emulation == "full":
+        st, own, packed_all, rows_of, lp, lp_ptrs, live = setup_gpu(w, device)
+        own_out = packed_all[w.rank]
+    else:
+        st, own, own_out, rows_of, lp, lp_ptrs, live = setup_gpu_rows(w, device)
     _, own_ptrs = own
-    own_out = packed_all[w.rank]
     b1, b2 = w.betas
     phases = ("pack", "reduce", "adam", "unpack")
 
@@ -340,7 +409,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, help="workload: 2 = GPT-2 1.5B-shaped list (default)")
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5),
+                    help="workload: 2 = GPT-2 1.5B-shaped list (the default and the reported line); 3 Llama-7B, "
+                         "4 7.5B paper-style at Nd=64, 5 ragged at Nd=1024 (informational)")
     ap.add_argument("--cpu-sample-elems", type=int, default=1_600_000_000,
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -356,9 +427,6 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU reduce-scatter/all-gather path is not built)", file=sys.stderr)
         sys.exit(2)
-    if args.config != 2:
-        print("bench.py: only the default workload (--config 2, GPT-2 1.5B-shaped list) is timed", file=sys.stderr)
-        sys.exit(2)
     import workloads as W
 
     w = W.workload(args.config)
@@ -373,7 +441,7 @@ def main():
                       "GBs": round(ab[p] / (per_phase[p] * 1e-3) / 1e9, 1),
                       "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     dom = max(kernels, key=lambda p: kernels[p]["ms"])
-    workload = "gpt2-1.5b-nd8-r0"
+    workload = WORKLOAD_IDS[args.config]
     traffic = measured_traffic(dom, workload)
     d = kernels[dom]
     out = {
@@ -389,12 +457,12 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "GPT-2 1.5B-shaped parameter list (48 layers, d=1600, vocab 50257, 1024 positions); "
-                               "Nd=8 virtual ranks, rank 0, 500M-element buckets; bf16 grads N(0,1e-3) and params, "
-                               "fp32 master N(0,0.02) / m / v; Adam lr 1e-3, betas (0.9, 0.999), eps 1e-8",
+        "config": {"workload": WORKLOAD_TEXT[args.config],
                    "workload_id": workload, "nd": w.nd, "rank": w.rank, "n_params": w.n,
                    "psi": int(sum(s * w.nd for s in shard_sizes)), "shard_elems": ab["shard_live"],
-                   "n_buckets": launches["pack"], "storage": "bf16 grads/params, fp32 state"},
+                   "n_buckets": launches["pack"],
+                   "storage": ("bf16" if w.dtype == W.BF16 else "fp16") + " grads/params, fp32 state",
+                   "emulation": w.emulation},
         "elem_per_s": round(ab["shard_live"] / (ms * 1e-3), 1),
         "grad_elem_per_s": round(ab["numel_live"] / (ms * 1e-3), 1),
         "step_bytes": step_bytes,
@@ -408,7 +476,7 @@ def main():
         "copy_reference_GBs": copy_reference(device),
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config == 2:
         log("[bench] timing the oracle on the host (cpu_baseline) ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_elems)
     print(json.dumps(out), flush=True)

@@ -23,8 +23,11 @@ namespace zs {
 #ifndef ZS_PACK_ROWS
 #define ZS_PACK_ROWS 2
 #endif
+#ifndef ZS_UNPACK_UNIFORM_K
+#define ZS_UNPACK_UNIFORM_K 1
+#endif
 #ifndef ZS_UNPACK_UNROLL
-#define ZS_UNPACK_UNROLL 1
+#define ZS_UNPACK_UNROLL 2
 #endif
 constexpr int kPackRows = ZS_PACK_ROWS;          // rows per block iteration of the pack
 constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
@@ -76,6 +79,74 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
     }
 }
 
+// Tiles holding several parameters: the block stages the fields of every parameter that
+// overlaps the tile in LDS once, and each thread finds its chunk's parameter there (a binary
+// search in LDS instead of dependent global loads).  Tiles touching more than kStageMax
+// parameters use the unstaged generic path.
+#ifndef ZS_STAGE_MAX
+#define ZS_STAGE_MAX 256
+#endif
+constexpr int kStageMax = ZS_STAGE_MAX;
+struct PackMeta {
+    int64_t off, end, s, numel;
+    const uint16_t* g;
+};
+
+// First staged index t in [0, cnt] with sm[t].end > x.
+__device__ __forceinline__ int staged_search(const PackMeta* sm, int cnt, int64_t x) {
+    int lo = 0, hi = cnt;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sm[mid].end > x) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, int t0, int64_t k, int64_t x,
+                                                  uint16_t* dst) {
+    if (t0 < cnt && sm[t0].off <= x && x + kChunk <= sm[t0].end) {
+        const PackMeta& m = sm[t0];
+        if (!m.g) return;  // no gradient this step
+        const int64_t e0 = k * m.s + (x - m.off);
+        uint4 v;
+        if (e0 + kChunk <= m.numel && aligned16(m.g)) {
+            v = load8_realigned(m.g, e0);
+        } else {
+            const ZS_GLOBAL uint16_t* gg = gptr(m.g);
+            uint16_t h[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) h[t] = (e0 + t < m.numel) ? gg[e0 + t] : uint16_t(0);
+            v = pack8(h);
+        }
+        store16(dst, v);
+        return;
+    }
+    uint16_t h[8];
+    unsigned keep = 0;
+    int i = t0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int64_t xt = x + t;
+        while (i < cnt && sm[i].end <= xt) ++i;
+        h[t] = 0;
+        if (i < cnt && sm[i].off <= xt) {
+            const uint16_t* g = sm[i].g;
+            if (!g) continue;
+            const int64_t e = k * sm[i].s + (xt - sm[i].off);
+            if (e < sm[i].numel) h[t] = gptr(g)[e];
+        }
+        keep |= 1u << t;
+    }
+    if (keep == 0xffu) {
+        store16(dst, pack8(h));
+    } else {
+        ZS_GLOBAL uint16_t* d = gptr(dst);
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            if (keep & (1u << t)) d[t] = h[t];
+    }
+}
+
 // Work item w = (tile, group of kPackRows rows) of the bucket, rows varying fastest (on MI355X
 // this dispatch order streams faster than tile-fastest).  When the whole tile lies inside one
 // parameter with a 16-byte aligned gradient (decided once per block from scalar loads), each
@@ -84,6 +155,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
                                                       int64_t n_tile, int64_t n_rg,
                                                       const uint16_t* const* __restrict__ grads,
                                                       uint16_t* __restrict__ packed) {
+    __shared__ PackMeta sm[kStageMax];
     const int64_t n_work = n_tile * n_rg;
     for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         int64_t jt;
@@ -131,6 +203,23 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
             }
             continue;
         }
+        // parameters overlapping the tile: [iu, last], last = the tile map's next entry (clamped)
+        const int64_t inext = ld_const(P.tile_first, j + 1);
+        const int64_t last = inext < P.n ? inext : P.n - 1;
+        const int64_t cnt = iu < P.n ? last - iu + 1 : 0;
+        if (cnt <= kStageMax) {
+            __syncthreads();  // the previous iteration's readers are done with the stage
+            for (int64_t t = threadIdx.x; t < cnt; t += kBlock) {
+                const int64_t pi = iu + t;
+                sm[t] = PackMeta{P.off[pi], P.end[pi], P.s[pi], P.numel[pi], grads[pi]};
+            }
+            __syncthreads();
+            if (x < b_base || x >= b_base + b_stride) continue;
+            const int t0 = staged_search(sm, int(cnt), x);
+            for (int64_t k = k0; k < kend; ++k)
+                pack_chunk_staged(sm, int(cnt), t0, k, x, packed + k * b_stride + (x - b_base));
+            continue;
+        }
         if (x < b_base || x >= b_base + b_stride) continue;
         const int64_t i = param_of_column(P, x);
         for (int64_t k = k0; k < kend; ++k) pack_chunk_generic(P, i, k, x, grads, packed + k * b_stride + (x - b_base));
@@ -138,39 +227,62 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
 }
 
 // ----------------------------------------------------------------------------- unpack --
-// Generic per-thread unpack of chunk u (parameter boundaries, row crossings, tails,
-// unaligned outputs).
-__device__ __forceinline__ void unpack_chunk_generic(const DevPlan& P, int64_t u, int64_t b_base, int64_t b_stride,
-                                                     const uint16_t* __restrict__ gathered,
-                                                     uint16_t* const* __restrict__ outs) {
-    const int64_t i = param_of_chunk(P, u);
-    uint16_t* out = outs[i];
-    if (!out) return;
-    const int64_t numel = P.numel[i], s = P.s[i];
-    const int64_t col = P.off[i] - b_base;
-    const int64_t e0 = (u - P.ucb[i]) * kChunk;
+// Elements 0..split-1 of a followed by elements 0..7-split of b.
+__device__ __forceinline__ uint4 merge_split(const uint4& a, const uint4& b, int split) {
+    uint16_t h[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[t] = t < split ? elem_of(a, t) : elem_of(b, (t - split) & 7);
+    return pack8(h);
+}
+
+// One chunk of parameter fields (numel, s, column of the slice in the rows, 1/s, chunk base).
+// Element e0..e0+7 of the parameter: row k = e0 / s, column j0 = e0 mod s.  A chunk inside one
+// row is one realigned load; a chunk crossing into the next row (s >= 8) is two realigned
+// loads and a merge (a crossing chunk is never in the last row, so both loads stay inside
+// the block); the tail of a parameter and rows shorter than 8 go element by element.
+__device__ __forceinline__ void unpack_chunk(int64_t u, int64_t ucb, int64_t numel, int64_t s, int64_t col,
+                                             double inv_s, int64_t b_stride, const uint16_t* __restrict__ gathered,
+                                             uint16_t* out) {
+    const int64_t e0 = (u - ucb) * kChunk;
     // row k = e0 / s and column j0 = e0 mod s; the double estimate is off by at most one
-    int64_t k = int64_t(double(e0) * P.inv_s[i]);
+    int64_t k = int64_t(double(e0) * inv_s);
     int64_t j0 = e0 - k * s;
     if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
-    if (e0 + kChunk <= numel && j0 + kChunk <= s && aligned16(out)) {
-        store16(out + e0, load8_realigned(gathered, k * b_stride + col + j0));
-    } else {
-        const int cnt = int(numel - e0 < kChunk ? numel - e0 : kChunk);
-        ZS_GLOBAL uint16_t* o = gptr(out);
-        const ZS_GLOBAL uint16_t* gsrc = gptr(gathered);
-        for (int t = 0; t < cnt; ++t) {
-            o[e0 + t] = gsrc[k * b_stride + col + j0];
-            if (++j0 == s) { j0 = 0; ++k; }
+    if (e0 + kChunk <= numel && aligned16(out)) {
+        if (j0 + kChunk <= s) {
+            store16(out + e0, load8_realigned(gathered, k * b_stride + col + j0));
+            return;
         }
+        if (s >= kChunk) {
+            const uint4 a = load8_realigned(gathered, k * b_stride + col + j0);
+            const uint4 b = load8_realigned(gathered, (k + 1) * b_stride + col);
+            store16(out + e0, merge_split(a, b, int(s - j0)));
+            return;
+        }
+    }
+    const int cnt = int(numel - e0 < kChunk ? numel - e0 : kChunk);
+    ZS_GLOBAL uint16_t* o = gptr(out);
+    const ZS_GLOBAL uint16_t* gsrc = gptr(gathered);
+    for (int t = 0; t < cnt; ++t) {
+        o[e0 + t] = gsrc[k * b_stride + col + j0];
+        if (++j0 == s) { j0 = 0; ++k; }
     }
 }
 
+struct UnpackMeta {
+    int64_t ucb, ucend, numel, s, col;
+    double inv_s;
+    uint16_t* out;
+};
+
 // One block iteration covers kUnpackUnroll consecutive chunk tiles (256 chunks each); a
-// thread takes one chunk of each.  Chunks of the bucket's parameters are [u0, u1).
+// thread takes one chunk of each.  Chunks of the bucket's parameters are [u0, u1).  A group
+// inside one parameter reads that parameter's fields once (scalar loads); otherwise the block
+// stages the fields of every overlapping parameter in LDS (up to kStageMax of them).
 __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t u0,
                                                         int64_t u1, const uint16_t* __restrict__ gathered,
                                                         uint16_t* const* __restrict__ outs) {
+    __shared__ UnpackMeta sm[kStageMax];
     const int64_t ut0 = u0 >> kUTileShift;
     const int64_t n_ut = ((u1 + kUTileChunks - 1) >> kUTileShift) - ut0;
     const int64_t n_groups = (n_ut + kUnpackUnroll - 1) / kUnpackUnroll;
@@ -187,34 +299,71 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_bas
         const double inv_s = ld_const(P.inv_s, ic);
         uint16_t* const out = ld_const(outs, ic);
         const bool whole = ua >= u0 && ub <= u1 && iu < P.n && ucb <= ua && ucend >= ub;
-        if (whole && !out) continue;  // every chunk of the group belongs to a skipped parameter
-        if (whole && aligned16(out)) {
-            // every chunk of the group belongs to parameter iu
-            uint4 v[kUnpackUnroll];
-            int64_t e[kUnpackUnroll];
-            bool ok[kUnpackUnroll];
+        if (whole) {
+            if (!out) continue;  // every chunk of the group belongs to a skipped parameter
+#if ZS_UNPACK_UNIFORM_K
+            // Rows at least as long as the group: find the group's first row once per block;
+            // each thread's chunk is then in that row or the next.
+            constexpr int64_t kSpanElems = kUnpackUnroll * kUTileChunks * kChunk;
+            if (s >= kSpanElems && aligned16(out)) {
+                const int64_t es = (ua - ucb) * kChunk;
+                int64_t ks = int64_t(double(es) * inv_s);
+                int64_t js = es - ks * s;
+                if (js < 0) { --ks; js += s; } else if (js >= s) { ++ks; js -= s; }
+#pragma unroll
+                for (int t = 0; t < kUnpackUnroll; ++t) {
+                    const int64_t d = (int64_t(t) * kUTileChunks + threadIdx.x) * kChunk;
+                    const int64_t e0 = es + d;
+                    int64_t j0 = js + d, k = ks;
+                    if (j0 >= s) { j0 -= s; ++k; }
+                    if (e0 + kChunk <= numel && j0 + kChunk <= s)
+                        store16(out + e0, load8_realigned(gathered, k * b_stride + col + j0));
+                    else
+                        unpack_chunk(ua + t * kUTileChunks + threadIdx.x, ucb, numel, s, col, inv_s, b_stride,
+                                     gathered, out);
+                }
+                continue;
+            }
+#endif
+#pragma unroll
+            for (int t = 0; t < kUnpackUnroll; ++t)
+                unpack_chunk(ua + t * kUTileChunks + threadIdx.x, ucb, numel, s, col, inv_s, b_stride, gathered, out);
+            continue;
+        }
+        // parameters overlapping the group: [iu, last]
+        const int64_t unext = ut + kUnpackUnroll <= P.n_utiles ? ut + kUnpackUnroll : P.n_utiles;
+        const int64_t inext = ld_const(P.utile_first, unext);
+        const int64_t last = inext < P.n ? inext : P.n - 1;
+        const int64_t cnt = iu < P.n ? last - iu + 1 : 0;
+        if (cnt <= kStageMax) {
+            __syncthreads();  // the previous iteration's readers are done with the stage
+            for (int64_t t = threadIdx.x; t < cnt; t += kBlock) {
+                const int64_t pi = iu + t;
+                sm[t] = UnpackMeta{P.ucb[pi], P.ucend[pi], P.numel[pi], P.s[pi], P.off[pi] - b_base, P.inv_s[pi],
+                                   outs[pi]};
+            }
+            __syncthreads();
 #pragma unroll
             for (int t = 0; t < kUnpackUnroll; ++t) {
                 const int64_t u = ua + t * kUTileChunks + threadIdx.x;
-                const int64_t e0 = (u - ucb) * kChunk;
-                int64_t k = int64_t(double(e0) * inv_s);
-                int64_t j0 = e0 - k * s;
-                if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
-                e[t] = e0;
-                ok[t] = e0 + kChunk <= numel && j0 + kChunk <= s;
-                if (ok[t]) v[t] = load8_realigned(gathered, k * b_stride + col + j0);
-            }
-#pragma unroll
-            for (int t = 0; t < kUnpackUnroll; ++t) {
-                if (ok[t]) store16(out + e[t], v[t]);
-                else unpack_chunk_generic(P, ua + t * kUTileChunks + threadIdx.x, b_base, b_stride, gathered, outs);
+                if (u < u0 || u >= u1) continue;
+                int lo = 0, hi = int(cnt);  // first staged parameter with ucend > u
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (sm[mid].ucend > u) hi = mid; else lo = mid + 1;
+                }
+                const UnpackMeta& m = sm[lo];
+                if (m.out) unpack_chunk(u, m.ucb, m.numel, m.s, m.col, m.inv_s, b_stride, gathered, m.out);
             }
             continue;
         }
 #pragma unroll
         for (int t = 0; t < kUnpackUnroll; ++t) {
             const int64_t u = ua + t * kUTileChunks + threadIdx.x;
-            if (u >= u0 && u < u1) unpack_chunk_generic(P, u, b_base, b_stride, gathered, outs);
+            if (u < u0 || u >= u1) continue;
+            const int64_t i = param_of_chunk(P, u);
+            uint16_t* o = outs[i];
+            if (o) unpack_chunk(u, P.ucb[i], P.numel[i], P.s[i], P.off[i] - b_base, P.inv_s[i], b_stride, gathered, o);
         }
     }
 }
