@@ -421,7 +421,7 @@ def main():
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
     if args.summarize_profiles:
-        print(summarize_profiles(args.summarize_profiles, "gpt2-1.5b-nd8-r0", args.profile_command), end="")
+        print(summarize_profiles(args.summarize_profiles, WORKLOAD_IDS[args.config], args.profile_command), end="")
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
