@@ -54,7 +54,8 @@ def algorithmic_bytes(numels, shard_sizes, live, nd):
     """Bytes each stage must move, per the method (not what the kernels happen to move):
     pack 2 B read per gradient element + 2 B written per padded element; reduce Nd 16-bit
     reads + one fp32 write per shard element; Adam 16 B read (g, p, m, v) + 14 B written
-    (p, m, v, 16-bit param) per shard element; unpack 2 B read + 2 B written per element."""
+    (p, m, v, 16-bit param) per shard element; unpack 2 B read + 2 B written per element.
+    The fused reduce + Adam: Nd 16-bit reads + 12 B read (p, m, v) + 14 B written per shard element."""
     numel_live = int(sum(int(n) for n, l in zip(numels, live) if l))
     padded_live = int(sum(int(s) * nd for s, l in zip(shard_sizes, live) if l))
     shard_live = int(sum(int(s) for s, l in zip(shard_sizes, live) if l))
@@ -63,6 +64,7 @@ def algorithmic_bytes(numels, shard_sizes, live, nd):
         "pack": 2 * numel_live + 2 * padded_live,
         "reduce": (2 * nd + 4) * shard_live,
         "adam": 30 * shard_live,
+        "reduce_adam": (2 * nd + 26) * shard_live,
         "unpack": 4 * numel_all,
         "shard_live": shard_live,
         "numel_live": numel_live,
@@ -189,37 +191,49 @@ def setup_gpu_rows(w, device):
     return st, (gl, own_ptrs), st.packed, rows_of, lp, lp_ptrs, live
 
 
-def run_gpu(w, steps, warmup, device):
+def setup(w, device):
     if w.emulation == "full":
         st, own, packed_all, rows_of, lp, lp_ptrs, live = setup_gpu(w, device)
         own_out = packed_all[w.rank]
     else:
         st, own, own_out, rows_of, lp, lp_ptrs, live = setup_gpu_rows(w, device)
-    _, own_ptrs = own
+    return st, own[1], own_out, rows_of, lp, lp_ptrs, live
+
+
+PHASES = {"unfused": ("pack", "reduce", "adam", "unpack"), "fused": ("pack", "reduce_adam", "unpack")}
+
+
+def run_gpu(w, ctx, path, steps, warmup):
+    """Time `steps` steps of one path.  unfused: pack -> reduce with the fused overflow check
+    -> Adam -> unpack; fused: pack with the input check -> per-parameter step sizes + per-bucket
+    reduce + Adam in one kernel -> unpack."""
+    st, own_ptrs, own_out, rows_of, lp, lp_ptrs, live = ctx
     b1, b2 = w.betas
-    phases = ("pack", "reduce", "adam", "unpack")
+    phases = PHASES[path]
 
     def one_step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        st.pack(own_ptrs, out=own_out)
-        if ev is not None:
-            ev[1].record()
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+
+        mark(0)
         st.flag.zero_()
-        st.reduce(rows_of, fused_check=True)
-        if ev is not None:
-            ev[2].record()
-        st.adam(w.lr, b1, b2, w.eps, w.grad_scale)
-        if ev is not None:
-            ev[3].record()
+        st.pack(own_ptrs, out=own_out, check=(path == "fused"))
+        mark(1)
+        if path == "unfused":
+            st.reduce(rows_of, fused_check=True)
+            mark(2)
+            st.adam(w.lr, b1, b2, w.eps, w.grad_scale)
+        else:
+            st.reduce_adam(rows_of, w.lr, b1, b2, w.eps, w.grad_scale)
+        mark(len(phases) - 1)
         st.unpack(lp_ptrs)
-        if ev is not None:
-            ev[4].record()
+        mark(len(phases))
 
     for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -231,12 +245,12 @@ def run_gpu(w, steps, warmup, device):
         for j, p in enumerate(phases):
             per_phase[p] += ev[j].elapsed_time(ev[j + 1])
     per_phase = {p: v / steps for p, v in per_phase.items()}  # ms per step
-    # launches of each stage's streaming kernel (Adam's phase also holds its small per-parameter
-    # prepare kernel, a few microseconds)
-    launches = {"pack": len(st.buckets), "reduce": len(st.buckets), "adam": 1, "unpack": len(st.buckets)}
-    shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
+    # launches of each stage's streaming kernel (the Adam phases also hold the small
+    # per-parameter prepare kernel, a few microseconds; the pack phase a 4-byte fill)
+    nb = len(st.buckets)
+    launches = {"pack": nb, "reduce": nb, "adam": 1, "reduce_adam": nb, "unpack": nb}
     flag = int(st.flag.item())
-    return wall / steps * 1e3, per_phase, launches, shard_sizes, flag
+    return wall / steps * 1e3, per_phase, {p: launches[p] for p in phases}, flag
 
 
 def copy_reference(device, nbytes=2 << 30, reps=10):
@@ -431,15 +445,28 @@ def main():
 
     w = W.workload(args.config)
     device = torch.device("cuda:0")
-    ms, per_phase, launches, shard_sizes, flag = run_gpu(w, args.steps, args.warmup, device)
+    ctx = setup(w, device)
+    st = ctx[0]
+    shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
     live = W.live_mask(w, 0)
     ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
-    step_bytes = ab["pack"] + ab["reduce"] + ab["adam"] + ab["unpack"]
-    kernels = {}
-    for p in ("pack", "reduce", "adam", "unpack"):
-        kernels[p] = {"ms": round(per_phase[p], 4), "launches": launches[p], "bytes": ab[p],
-                      "GBs": round(ab[p] / (per_phase[p] * 1e-3) / 1e9, 1),
-                      "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    runs = {}
+    for path in ("unfused", "fused"):
+        ms_p, per_phase, launches, flag = run_gpu(w, ctx, path, args.steps, args.warmup)
+        kernels = {}
+        for p in PHASES[path]:
+            kernels[p] = {"ms": round(per_phase[p], 4), "launches": launches[p], "bytes": ab[p],
+                          "GBs": round(ab[p] / (per_phase[p] * 1e-3) / 1e9, 1),
+                          "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        runs[path] = dict(ms=ms_p, kernels=kernels, launches=launches, flag=flag,
+                          bytes=sum(ab[p] for p in PHASES[path]))
+    ms, kernels, launches, flag = (runs["unfused"][k] for k in ("ms", "kernels", "launches", "flag"))
+    step_bytes = runs["unfused"]["bytes"]
+    fz = runs["fused"]
+    fused = {"ms_per_step": round(fz["ms"], 4), "speedup": round(ms / fz["ms"], 3),
+             "GBs": round(fz["bytes"] / (fz["ms"] * 1e-3) / 1e9, 1), "step_bytes": fz["bytes"],
+             "elem_per_s": round(ab["shard_live"] / (fz["ms"] * 1e-3), 1), "overflow_flag": fz["flag"],
+             "kernels": fz["kernels"]}
     dom = max(kernels, key=lambda p: kernels[p]["ms"])
     workload = WORKLOAD_IDS[args.config]
     traffic = measured_traffic(dom, workload)
@@ -468,6 +495,7 @@ def main():
         "step_bytes": step_bytes,
         "overflow_flag": flag,
         "kernels": kernels,
+        "fused": fused,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["bytes"] / launches[dom] /
                                                                       (d["ms"] / launches[dom] * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],

@@ -251,6 +251,55 @@ zero_status zero_unpack(const zero_plan* plan, int64_t b, const void* d_gathered
 zero_status zero_shard_init(const zero_plan* plan, const void* const* d_src_ptrs, int32_t src_dtype, float* d_p32,
                             void* stream);
 
+/* ------------------------------------------- fused path: reduce + check + Adam ------ */
+/* The same step with the reduced gradient kept in registers: the sum of the Nd rows goes
+ * straight into the Adam update, so the fp32 gradient shard is neither written nor read.
+ * Because the step must be skipped before any state changes, the overflow verdict comes
+ * from the inputs rather than from the sums.  Per step, on one stream:
+ *   1. *d_flag = 0; zero_pack_bucket_check for every bucket (this rank's gradients);
+ *   2. the ranks OR their flags (an all-reduce of one int; nothing to do on one process);
+ *   3. zero_adam_prepare (step counts and step sizes, or nothing if the flag is set);
+ *   4. per bucket, once its rows have arrived: zero_reduce_adam_bucket.
+ * With the flag clear, p32, m, v, the step counts and the 16-bit parameters are
+ * bit-identical to zero_reduce_shard + zero_adam_step on the same rows. */
+
+/* zero_pack_bucket, and OR 1 into *d_flag when a gradient element that the call reads is
+ * inf or NaN or has |x| > 2^126 / Nd.  Below that bound no fp32 sum of Nd such values can
+ * overflow (each term is below 2^126 / Nd, so every partial sum stays below 2^126), so a flag
+ * that is clear on every rank means every reduced sum is finite.  A finite value above the
+ * bound flags the step although the sums might not overflow: a conservative skip, which
+ * needs |g| near 2^126 / Nd (never reached by fp16; for bf16 a scaled gradient already
+ * beyond any usable loss scale).  Never clears the flag.
+ *   d_flag   device int32
+ * Errors: as zero_pack_bucket, and ZERO_EINVAL for d_flag == NULL. */
+zero_status zero_pack_bucket_check(const zero_plan* plan, int64_t b, const void* const* d_grad_ptrs,
+                                   void* d_packed, int32_t* d_flag, void* stream);
+
+/* The first launch of zero_adam_step on its own: if d_flag is NULL or *d_flag == 0, every
+ * live parameter's step count advances and its step size lr / (1 - beta1^t) and
+ * 1 / sqrt(1 - beta2^t) are stored in the plan (double, rounded to fp32 once), with the fp32
+ * hyperparameters; if the flag is set, nothing changes.  The stored values serve the
+ * zero_reduce_adam_bucket calls that follow on the same stream; the plan holds one set, so
+ * do not interleave two steps of one plan on different streams.
+ * Errors: ZERO_EINVAL as for zero_adam_step. */
+zero_status zero_adam_prepare(const zero_plan* plan, const uint8_t* d_live, int32_t* d_steps,
+                              const zero_adam_hparams* hp, const int32_t* d_flag, void* stream);
+
+/* Reduce bucket b and take the Adam step on its columns in one pass [LLZ BWD reduce-scatter,
+ * then LLZ Optim on the matching shard; Z3 ZeRO-1/2 all-gather row]: for every column c of a
+ * live parameter of the bucket, acc is formed as in zero_reduce_shard and used as g32 in the
+ * update of zero_adam_step, which writes p32, m, v at O_b + c and the 16-bit parameter at
+ * arena[Nd*O_b + r*L_b + c].  Dead parameters and the row gap are not touched.  If d_flag is
+ * not NULL and *d_flag != 0 nothing is written.  Needs zero_adam_prepare earlier on the same
+ * stream in this step, with the same d_live and d_flag.
+ *   d_rows, row_stride   as zero_reduce_shard
+ *   d_p32, d_m, d_v      device float[shard_numel], 16-byte aligned
+ *   d_arena              device 16-bit [Nd * shard_numel], 16-byte aligned
+ * Errors: ZERO_EINVAL for bad index, NULL/misaligned pointers or row_stride. */
+zero_status zero_reduce_adam_bucket(const zero_plan* plan, int64_t b, const void* d_rows, int64_t row_stride,
+                                    const uint8_t* d_live, float* d_p32, float* d_m, float* d_v,
+                                    const int32_t* d_flag, void* d_arena, void* stream);
+
 /* Thread-local text of the last error ("" if none). */
 const char* zero_last_error(void);
 

@@ -63,6 +63,8 @@ def lib():
         L.oracle_reduce_bucket.restype = None
         L.oracle_reduce_bucket.argtypes = [vp, vp, i64, i64, vp, i64, i32, vp, vp]
         L.oracle_overflow.restype = i32
+        L.oracle_input_check.restype = i32
+        L.oracle_input_check.argtypes = [vp, vp, i64, i64, vp, i32]
         L.oracle_overflow.argtypes = [vp, i64, vp, vp]
         L.oracle_adam_element.restype = None
         L.oracle_adam_element.argtypes = [ctypes.c_float, vp, vp, vp, i64, dbl, dbl, dbl, dbl, dbl]
@@ -159,6 +161,13 @@ def reduce_bucket(pl: Plan, b: int, rows: np.ndarray, dtype: int, live: np.ndarr
 def overflow(pl: Plan, g32: np.ndarray, live: np.ndarray) -> int:
     live = np.ascontiguousarray(live, dtype=np.uint8)
     return int(lib().oracle_overflow(_ptr(pl.params), pl.n, _ptr(g32), _ptr(live)))
+
+
+def input_check(pl: Plan, b: int, grads, dtype: int) -> int:
+    """Verdict of the fused path's input check over bucket b's gradients (list, None = no gradient)."""
+    keep = [None if g is None else np.ascontiguousarray(g, dtype=np.uint16) for g in grads]
+    table = _ptr_table(keep)
+    return int(lib().oracle_input_check(_ptr(pl.params), _ptr(pl.buckets), pl.nd, b, _ptr(table), dtype))
 
 
 @dataclass

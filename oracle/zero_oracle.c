@@ -274,6 +274,30 @@ int oracle_overflow(const int64_t* params, int64_t n, const float* g32, const ui
     return flag;
 }
 
+/*
+ * The input-side verdict of the fused path (a reading: the pages do not treat overflow).  1 if
+ * a gradient element of a parameter of bucket b that has a gradient (grads[i] != NULL) is inf
+ * or NaN, or if |x| * nd > 2^126.  The product of a 16-bit value (at most 11 significant bits)
+ * and nd (at most 16 bits) is exact in double, so the comparison is exact.  Padding is not a
+ * gradient element and is not examined.
+ */
+int oracle_input_check(const int64_t* params, const int64_t* buckets, int64_t nd, int64_t b,
+                       const uint16_t* const* grads, int dtype) {
+    const int64_t* bk = buckets + b * ORB_NFIELDS;
+    const double limit = ldexp(1.0, 126);
+    int flag = 0;
+    for (int64_t i = bk[ORB_FIRST]; i < bk[ORB_FIRST] + bk[ORB_COUNT]; i++) {
+        const uint16_t* g = grads[i];
+        if (g == NULL) continue;
+        const int64_t numel = params[i * ORP_NFIELDS + ORP_NUMEL];
+        for (int64_t e = 0; e < numel; e++) {
+            double x = (double)to_f32(g[e], dtype);
+            if (!isfinite(x) || fabs(x) * (double)nd > limit) flag = 1;
+        }
+    }
+    return flag;
+}
+
 /* ------------------------------------------------------------------ Adam (O5) ------ */
 /*
  * One element of textbook Adam (bias-corrected, no weight decay), in double from the

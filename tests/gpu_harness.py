@@ -55,18 +55,22 @@ def assert_close_f32(got: np.ndarray, want: np.ndarray, what: str, rel=1e-6, abs
                              f"want {want[i]!r}")
 
 
-def ordered16(h: np.ndarray) -> np.ndarray:
-    """Integers in the order of the 16-bit float values (sign-magnitude to two's complement)."""
-    h = h.astype(np.int64)
-    return np.where(h < 0x8000, h, -(h & 0x7FFF))
-
-
-def assert_within_ulp16(got: np.ndarray, want: np.ndarray, what: str, ulps: int = 1) -> None:
-    d = np.abs(ordered16(got) - ordered16(want))
-    if (d > ulps).any():
-        i = np.flatnonzero(d > ulps)[0]
-        raise AssertionError(f"{what}: {np.count_nonzero(d > ulps)} beyond {ulps} ulp; first at {i}: "
-                             f"got {got[i]:#06x} want {want[i]:#06x}")
+def expected_arena(pl: oracle.Plan, oracle_arena: np.ndarray, got_p32: np.ndarray, ever: np.ndarray,
+                   dtype: int) -> np.ndarray:
+    """The arena the Adam step must leave: the oracle's everywhere, except at row r of every
+    bucket in the columns of parameters that have taken a step, which hold the 16-bit RNE (by the
+    oracle's conversion) of the kernel's own p32 -- the write is defined as that rounding, and
+    the kernel's p32 is checked against the oracle's separately.  (Near zero the p32 tolerance
+    can exceed a 16-bit ulp, so a 1-ulp bound on the 16-bit value against the oracle would not
+    follow from it.)"""
+    want = oracle_arena.copy()
+    lp = oracle.from_f32(got_p32.astype(np.float32), dtype)
+    for b in range(pl.n_buckets):
+        O, L = int(pl.buckets[b, oracle.B_BASE]), int(pl.buckets[b, oracle.B_STRIDE])
+        row = want[pl.nd * O + pl.rank * L: pl.nd * O + pl.rank * L + L]
+        sel = ever[O:O + L]
+        row[sel] = lp[O:O + L][sel]
+    return want
 
 
 def ragged_numels(rng: np.random.Generator, n: int, nd: int, hi: int) -> list:
@@ -114,3 +118,65 @@ def oracle_block(pl: oracle.Plan, flat: np.ndarray, b: int) -> np.ndarray:
     off = pl.nd * pl.buckets[b, oracle.B_BASE]
     L = pl.buckets[b, oracle.B_STRIDE]
     return flat[off:off + pl.nd * L].reshape(pl.nd, L)
+
+
+# ------------------------------------------------ sampling at full size ---------------
+P_OFF, P_S, P_NUMEL, P_COL = oracle.P_OFFSET, oracle.P_SHARD, oracle.P_NUMEL, oracle.P_COL
+
+
+def sample_columns(pl, rng, count, extra_params=300):
+    """Shard columns inside parameter slices: uniform ones plus the first and last slice column
+    of some parameters (boundaries of parameters, buckets and padding)."""
+    s = pl.params[:, P_S]
+    cum = np.cumsum(s)
+    pick = rng.integers(0, cum[-1], size=count)
+    i = np.searchsorted(cum, pick, side="right")
+    j = pick - (cum[i] - s[i])
+    cols = pl.params[i, P_OFF] + j
+    nz = np.flatnonzero(s > 0)
+    chosen = rng.choice(nz, size=min(extra_params, nz.size), replace=False)
+    edges = np.concatenate([pl.params[chosen, P_OFF], pl.params[chosen, P_OFF] + s[chosen] - 1])
+    return np.unique(np.concatenate([cols, edges]))
+
+
+def column_owner(pl, cols):
+    """(param, index of the column inside the param's slice) for shard columns."""
+    ends = pl.params[:, P_OFF] + pl.params[:, P_S]
+    i = np.searchsorted(ends, cols, side="right")
+    return i, cols - pl.params[i, P_OFF]
+
+
+def gather_params(tensors, idx_i, idx_e, fill=0):
+    """Values tensors[i][e] for parallel index arrays (device gathers, one per parameter), on
+    the host; `fill` where e is past the parameter's end (padding) or the tensor is None."""
+    dt = next(t.dtype for t in tensors if t is not None)
+    out = torch.full((idx_i.size,), fill, dtype=dt)
+    for i in np.unique(idx_i):
+        t = tensors[i]
+        if t is None:
+            continue
+        sel = np.flatnonzero(idx_i == i)
+        e = idx_e[sel]
+        ok = e < t.numel()
+        if ok.any():
+            out[torch.from_numpy(sel[ok])] = t[torch.from_numpy(e[ok]).to(t.device)].cpu()
+    return out
+
+
+def bits16(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def row_zero_mask(pl, b, live):
+    """Positions of one rank row (rank r's row of bucket b) that a real packer sends as +0 or
+    leaves unwritten: padding of each parameter, dead parameters, and the row gap."""
+    L = int(pl.buckets[b, oracle.B_STRIDE])
+    keep = np.zeros(L, dtype=bool)
+    r = pl.rank
+    for i in pl.bucket_params(b):
+        if not live[i]:
+            continue
+        c, s_, n = pl.params[i, P_COL], pl.params[i, P_S], pl.params[i, P_NUMEL]
+        real = max(0, min(s_, n - r * s_))
+        keep[c:c + real] = True
+    return ~keep

@@ -83,6 +83,10 @@ def test_hot_calls_reject_null_plan(L):
                             None) == B.ZERO_EINVAL
     assert L.zero_unpack(None, 0, vp(16), vp(16), None) == B.ZERO_EINVAL
     assert L.zero_shard_init(None, vp(16), 0, vp(16), None) == B.ZERO_EINVAL
+    assert L.zero_pack_bucket_check(None, 0, vp(16), vp(16), vp(16), None) == B.ZERO_EINVAL
+    assert L.zero_adam_prepare(None, vp(16), vp(16), ctypes.byref(hp), None, None) == B.ZERO_EINVAL
+    assert L.zero_reduce_adam_bucket(None, 0, vp(16), 8, vp(16), vp(16), vp(16), vp(16), None, vp(16),
+                                     None) == B.ZERO_EINVAL
     s = B.zero_plan_summary()
     assert L.zero_plan_get_summary(None, ctypes.byref(s)) == B.ZERO_EINVAL
     L.zero_plan_destroy(None)  # no-op

@@ -17,8 +17,8 @@ import torch
 import oracle
 import workloads as W
 import zero_sharded_mixed_amd as Z
-from gpu_harness import (DEV, assert_close_f32, assert_same_f32, assert_within_ulp16, oracle_block, say, to_np16,
-                         to_np32)
+from gpu_harness import (DEV, assert_close_f32, assert_same_f32, bits16, column_owner, expected_arena, gather_params,
+                         oracle_block, row_zero_mask, sample_columns, say, to_np16, to_np32)
 
 pytestmark = pytest.mark.gpu
 P_OFF, P_S, P_NUMEL, P_COL, P_BUCKET, P_START = (oracle.P_OFFSET, oracle.P_SHARD, oracle.P_NUMEL, oracle.P_COL,
@@ -66,6 +66,7 @@ def test_mlp_model_every_element_three_steps():
     v = np.zeros_like(p32)
     steps = np.zeros(pl.n, np.int32)
     hp = oracle.AdamHP(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps, grad_scale=w.grad_scale)
+    ever = np.zeros(pl.shard_len, dtype=bool)  # columns of parameters that have taken a step
     packed_all = torch.zeros((nd, int(st.summary.arena_numel)), dtype=torch.int16, device=DEV)
     flat = packed_all.view(-1)
     for step in range(w.steps):
@@ -103,7 +104,9 @@ def test_mlp_model_every_element_three_steps():
         assert_close_f32(to_np32(st.p32), p32, f"p32 step {step}")
         assert_close_f32(to_np32(st.m), m, f"m step {step}")
         assert_close_f32(to_np32(st.v), v, f"v step {step}")
-        assert_within_ulp16(to_np16(st.arena), arena, f"arena step {step}")
+        for i in np.flatnonzero(live):
+            ever[pl.params[i, P_OFF]:pl.params[i, P_OFF] + pl.params[i, P_S]] = True
+        assert np.array_equal(to_np16(st.arena), expected_arena(pl, arena, to_np32(st.p32), ever, w.dtype)), step
         for i in (2, 3):  # the dropped layer: p32 / m / v bit-identical
             o, s_ = pl.params[i, P_OFF], pl.params[i, P_S]
             for old, t in zip(before, (st.p32, st.m, st.v)):
@@ -118,64 +121,6 @@ def test_mlp_model_every_element_three_steps():
 
 
 # ----------------------------------------------------------------- full-size workloads --
-
-def sample_columns(pl, rng, count, extra_params=300):
-    """Shard columns inside parameter slices: uniform ones plus the first and last slice column
-    of some parameters (boundaries of parameters, buckets and padding)."""
-    s = pl.params[:, P_S]
-    cum = np.cumsum(s)
-    pick = rng.integers(0, cum[-1], size=count)
-    i = np.searchsorted(cum, pick, side="right")
-    j = pick - (cum[i] - s[i])
-    cols = pl.params[i, P_OFF] + j
-    nz = np.flatnonzero(s > 0)
-    chosen = rng.choice(nz, size=min(extra_params, nz.size), replace=False)
-    edges = np.concatenate([pl.params[chosen, P_OFF], pl.params[chosen, P_OFF] + s[chosen] - 1])
-    return np.unique(np.concatenate([cols, edges]))
-
-
-def column_owner(pl, cols):
-    """(param, index of the column inside the param's slice) for shard columns."""
-    ends = pl.params[:, P_OFF] + pl.params[:, P_S]
-    i = np.searchsorted(ends, cols, side="right")
-    return i, cols - pl.params[i, P_OFF]
-
-
-def gather_params(tensors, idx_i, idx_e, fill=0):
-    """Values tensors[i][e] for parallel index arrays (device gathers, one per parameter), on
-    the host; `fill` where e is past the parameter's end (padding) or the tensor is None."""
-    dt = next(t.dtype for t in tensors if t is not None)
-    out = torch.full((idx_i.size,), fill, dtype=dt)
-    for i in np.unique(idx_i):
-        t = tensors[i]
-        if t is None:
-            continue
-        sel = np.flatnonzero(idx_i == i)
-        e = idx_e[sel]
-        ok = e < t.numel()
-        if ok.any():
-            out[torch.from_numpy(sel[ok])] = t[torch.from_numpy(e[ok]).to(t.device)].cpu()
-    return out
-
-
-def bits16(t):
-    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
-
-
-def row_zero_mask(pl, b, live):
-    """Positions of one rank row (rank r's row of bucket b) that a real packer sends as +0 or
-    leaves unwritten: padding of each parameter, dead parameters, and the row gap."""
-    L = int(pl.buckets[b, oracle.B_STRIDE])
-    keep = np.zeros(L, dtype=bool)
-    r = pl.rank
-    for i in pl.bucket_params(b):
-        if not live[i]:
-            continue
-        c, s_, n = pl.params[i, P_COL], pl.params[i, P_S], pl.params[i, P_NUMEL]
-        real = max(0, min(s_, n - r * s_))
-        keep[c:c + real] = True
-    return ~keep
-
 
 def run_fullsize(config, max_steps=None, n_samples=20000):
     w = W.workload(config)
@@ -324,7 +269,9 @@ def run_fullsize(config, max_steps=None, n_samples=20000):
         assert_close_f32(to_np32(st.v[cols_dev]), o_v, f"v step {step} (relative)", rel=2e-6, abs_=0.0)
         got_lp = bits16(st.arena[arena_rowr].cpu())
         ever_live = o_t[ci] > 0
-        assert_within_ulp16(got_lp[ever_live], oracle.from_f32(o_p32[ever_live], w.dtype), f"lp step {step}")
+        # the 16-bit parameter is the RNE of the kernel's own p32 (checked against the oracle above)
+        got_p = to_np32(st.p32[cols_dev])
+        assert np.array_equal(got_lp[ever_live], oracle.from_f32(got_p[ever_live], w.dtype)), f"lp step {step}"
         assert np.array_equal(got_lp[~ever_live], o_lp_before[~ever_live]), f"untouched lp step {step}"
         del own, own_ptrs
         if w.emulation != "full":

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_ENOMEM", -3: "ZERO_EH
 EXPORTS = ("zero_plan_create", "zero_plan_destroy", "zero_plan_get_summary", "zero_plan_param_info",
            "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes", "zero_pack_bucket",
            "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack", "zero_shard_init",
-           "zero_last_error")
+           "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket", "zero_last_error")
 
 
 class ZeroError(RuntimeError):
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
         "zero_adam_step": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
         "zero_unpack": (i32, [vp, i64, vp, vp, vp]),
         "zero_shard_init": (i32, [vp, vp, i32, vp, vp]),
+        "zero_pack_bucket_check": (i32, [vp, i64, vp, vp, vp, vp]),
+        "zero_adam_prepare": (i32, [vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp]),
+        "zero_reduce_adam_bucket": (i32, [vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "zero_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -213,6 +216,26 @@ def zero_unpack(plan: Plan, b: int, gathered: torch.Tensor, param_ptrs: torch.Te
 
 def zero_shard_init(plan: Plan, src_ptrs: torch.Tensor, src_dtype: int, p32: torch.Tensor, stream=None) -> None:
     _check(lib().zero_shard_init(plan.handle, _ptr(src_ptrs), src_dtype, _ptr(p32), _stream(stream)))
+
+
+def zero_pack_bucket_check(plan: Plan, b: int, grad_ptrs: torch.Tensor, packed: torch.Tensor, flag: torch.Tensor,
+                           stream=None) -> None:
+    _check(lib().zero_pack_bucket_check(plan.handle, b, _ptr(grad_ptrs), _ptr(packed), _ptr(flag), _stream(stream)))
+
+
+def zero_adam_prepare(plan: Plan, live: torch.Tensor, steps: torch.Tensor, lr: float, beta1: float, beta2: float,
+                      eps: float, grad_scale: float, flag: Optional[torch.Tensor], stream=None) -> None:
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale)
+    _check(lib().zero_adam_prepare(plan.handle, _ptr(live), _ptr(steps), ctypes.byref(hp), _ptr(flag),
+                                   _stream(stream)))
+
+
+def zero_reduce_adam_bucket(plan: Plan, b: int, rows: torch.Tensor, row_stride: int, live: torch.Tensor,
+                            p32: torch.Tensor, m: torch.Tensor, v: torch.Tensor, flag: Optional[torch.Tensor],
+                            arena: torch.Tensor, stream=None) -> None:
+    """rows as in zero_reduce_shard; needs zero_adam_prepare earlier in the step on the same stream."""
+    _check(lib().zero_reduce_adam_bucket(plan.handle, b, _ptr(rows), row_stride, _ptr(live), _ptr(p32), _ptr(m),
+                                         _ptr(v), _ptr(flag), _ptr(arena), _stream(stream)))
 
 
 def zero_last_error() -> str:

@@ -18,11 +18,9 @@
 // Both kernels return at once when the flag is set, so a skipped step changes nothing.
 #include <cmath>
 
-#include "zs_common.h"
+#include "zs_adam.h"
 
 namespace zs {
-
-enum AdamConst { AC_BETA1, AC_BETA2, AC_C1, AC_C2, AC_EPS, AC_GSCALE, kAdamConsts };
 
 __global__ void adam_prepare_kernel(DevPlan P, const uint8_t* __restrict__ live, int32_t* __restrict__ steps,
                                     const int32_t* __restrict__ flag, double lr, double beta1, double beta2, double eps,
@@ -59,35 +57,10 @@ struct AdamArgs {
     uint16_t* arena;
 };
 
-struct AdamK {
-    float b1, b2, c1, c2, eps, gs;
-};
-
-#ifndef ZS_ADAM_FAST_MATH
-#define ZS_ADAM_FAST_MATH 0
-#endif
-__device__ __forceinline__ void adam_elem(const AdamK& K, float g32, float& p, float& m, float& v, float step_size,
-                                          float inv_sqrt_bc2) {
-    const float g = g32 * K.gs;
-    m = K.b1 * m + K.c1 * g;
-    v = K.b2 * v + K.c2 * (g * g);
-#if ZS_ADAM_FAST_MATH
-    const float denom = __builtin_amdgcn_sqrtf(v) * inv_sqrt_bc2 + K.eps;
-    p = p - step_size * (m * __builtin_amdgcn_rcpf(denom));
-#else
-    const float denom = sqrtf(v) * inv_sqrt_bc2 + K.eps;
-    p = p - step_size * (m / denom);
-#endif
-}
-
 #ifndef ZS_ADAM_COLS
 #define ZS_ADAM_COLS 8
 #endif
 constexpr int kAdamCols = ZS_ADAM_COLS;  // shard columns per thread (4 or 8)
-
-template <int COLS> struct LpVec;
-template <> struct LpVec<4> { using T = uint2; };
-template <> struct LpVec<8> { using T = uint4; };
 
 // COLS consecutive columns of one live parameter: COLS/4 dwordx4 loads each of g, p, m, v;
 // COLS/4 dwordx4 stores each of p, m, v; one store of the COLS 16-bit parameters.
@@ -135,8 +108,7 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int
     if (A.flag && *A.flag) return;
     constexpr int64_t kSpan = int64_t(kBlock) * COLS;
     static_assert(kTileCols % kSpan == 0, "a span never crosses a tile");
-    const AdamK K{ld_const(A.consts, AC_BETA1), ld_const(A.consts, AC_BETA2), ld_const(A.consts, AC_C1),
-                  ld_const(A.consts, AC_C2),    ld_const(A.consts, AC_EPS),   ld_const(A.consts, AC_GSCALE)};
+    const AdamK K = load_adam_consts(A.consts);
     for (int64_t sp = blockIdx.x; sp < n_spans; sp += gridDim.x) {
         const int64_t x0 = sp * kSpan;
         const int64_t x = x0 + int64_t(threadIdx.x) * COLS;
@@ -189,6 +161,27 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int
 
 using namespace zs;
 
+namespace zs {
+zero_status launch_adam_prepare(const zero_plan* plan, const uint8_t* d_live, int32_t* d_steps,
+                                const zero_adam_hparams* hp, const int32_t* d_flag, hipStream_t s, const char* who) {
+    if (!d_live || !d_steps || !hp) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->grad_scale) || !(hp->beta1 >= 0.0) ||
+        !(hp->beta1 < 1.0) || !(hp->beta2 >= 0.0) || !(hp->beta2 < 1.0))
+        return fail(ZERO_EINVAL, "%s: hyperparameters out of range", who);
+    adam_prepare_kernel<<<grid_for((plan->n + 255) / 256, 1024), 256, 0, s>>>(
+        plan->dev, d_live, d_steps, d_flag, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->grad_scale,
+        reinterpret_cast<float2*>(plan->d_adam_scal), plan->d_adam_const);
+    return check_launch(who);
+}
+}  // namespace zs
+
+extern "C" zero_status zero_adam_prepare(const zero_plan* plan, const uint8_t* d_live, int32_t* d_steps,
+                                         const zero_adam_hparams* hp, const int32_t* d_flag, void* stream) {
+    zero_status st = check_device(plan);
+    if (st != ZERO_OK) return st;
+    return launch_adam_prepare(plan, d_live, d_steps, hp, d_flag, (hipStream_t)stream, "zero_adam_prepare");
+}
+
 extern "C" zero_status zero_adam_step(const zero_plan* plan, const float* d_g32, float* d_p32, float* d_m, float* d_v,
                                       const uint8_t* d_live, int32_t* d_steps, const zero_adam_hparams* hp,
                                       const int32_t* d_flag, void* d_arena, void* stream) {
@@ -199,15 +192,9 @@ extern "C" zero_status zero_adam_step(const zero_plan* plan, const float* d_g32,
     if (!host_aligned16(d_g32) || !host_aligned16(d_p32) || !host_aligned16(d_m) || !host_aligned16(d_v) ||
         !host_aligned16(d_arena))
         return fail(ZERO_EINVAL, "zero_adam_step: shard arrays and arena must be 16-byte aligned");
-    if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->grad_scale) || !(hp->beta1 >= 0.0) ||
-        !(hp->beta1 < 1.0) || !(hp->beta2 >= 0.0) || !(hp->beta2 < 1.0))
-        return fail(ZERO_EINVAL, "zero_adam_step: hyperparameters out of range");
     hipStream_t s = (hipStream_t)stream;
     float2* scal = reinterpret_cast<float2*>(plan->d_adam_scal);
-    adam_prepare_kernel<<<grid_for((plan->n + 255) / 256, 1024), 256, 0, s>>>(
-        plan->dev, d_live, d_steps, d_flag, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->grad_scale, scal,
-        plan->d_adam_const);
-    if ((st = check_launch("adam_prepare_kernel")) != ZERO_OK) return st;
+    if ((st = launch_adam_prepare(plan, d_live, d_steps, hp, d_flag, s, "zero_adam_step")) != ZERO_OK) return st;
     if (plan->shard_numel == 0) return ZERO_OK;
     AdamArgs A{d_g32, d_p32, d_m, d_v, d_live, scal, plan->d_adam_const, d_flag, static_cast<uint16_t*>(d_arena)};
     const int64_t span = int64_t(kBlock) * kAdamCols;

@@ -32,10 +32,26 @@ namespace zs {
 constexpr int kPackRows = ZS_PACK_ROWS;          // rows per block iteration of the pack
 constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
 
+// The input check of the checked pack: true if one of the eight 16-bit values is inf or NaN
+// or larger in magnitude than `limit` (2^126 / Nd: below it no fp32 sum of Nd values overflows).
+template <int DT>
+__device__ __forceinline__ bool out_of_range8(const uint4& v, float limit) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float lo = to_f32<DT>(w[t] & 0xffffu), hi = to_f32<DT>(w[t] >> 16);
+        bad |= !(fabsf(lo) <= limit) || !(fabsf(hi) <= limit);
+    }
+    return bad;
+}
+
 // Generic per-thread pack of one 8-column chunk of row k (parameter boundaries, padding,
 // row gaps, dead parameters, unaligned sources).  i is the first parameter with end > x.
+template <int DT, bool CHECK>
 __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, int64_t k, int64_t x,
-                                                   const uint16_t* const* __restrict__ grads, uint16_t* dst) {
+                                                   const uint16_t* const* __restrict__ grads, uint16_t* dst,
+                                                   float limit, bool& bad) {
     if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) {
         const uint16_t* g = grads[i];
         if (!g) return;  // no gradient this step: leave the slots alone
@@ -51,6 +67,7 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
             for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
             v = pack8(h);
         }
+        if constexpr (CHECK) bad |= out_of_range8<DT>(v, limit);
         store16(dst, v);
         return;
     }
@@ -69,6 +86,7 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
         }
         keep |= 1u << t;
     }
+    if constexpr (CHECK) bad |= out_of_range8<DT>(pack8(h), limit);
     if (keep == 0xffu) {
         store16(dst, pack8(h));
     } else {
@@ -102,8 +120,9 @@ __device__ __forceinline__ int staged_search(const PackMeta* sm, int cnt, int64_
     return lo;
 }
 
+template <int DT, bool CHECK>
 __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, int t0, int64_t k, int64_t x,
-                                                  uint16_t* dst) {
+                                                  uint16_t* dst, float limit, bool& bad) {
     if (t0 < cnt && sm[t0].off <= x && x + kChunk <= sm[t0].end) {
         const PackMeta& m = sm[t0];
         if (!m.g) return;  // no gradient this step
@@ -118,6 +137,7 @@ __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, i
             for (int t = 0; t < 8; ++t) h[t] = (e0 + t < m.numel) ? gg[e0 + t] : uint16_t(0);
             v = pack8(h);
         }
+        if constexpr (CHECK) bad |= out_of_range8<DT>(v, limit);
         store16(dst, v);
         return;
     }
@@ -137,6 +157,7 @@ __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, i
         }
         keep |= 1u << t;
     }
+    if constexpr (CHECK) bad |= out_of_range8<DT>(pack8(h), limit);
     if (keep == 0xffu) {
         store16(dst, pack8(h));
     } else {
@@ -151,12 +172,16 @@ __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, i
 // this dispatch order streams faster than tile-fastest).  When the whole tile lies inside one
 // parameter with a 16-byte aligned gradient (decided once per block from scalar loads), each
 // thread issues the loads of its rows before any store.
+// CHECK: also OR 1 into *flag when a gradient element is non-finite or above `limit`.
+template <int DT, bool CHECK>
 __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t tile0,
                                                       int64_t n_tile, int64_t n_rg,
                                                       const uint16_t* const* __restrict__ grads,
-                                                      uint16_t* __restrict__ packed) {
+                                                      uint16_t* __restrict__ packed, float limit,
+                                                      int32_t* __restrict__ flag) {
     __shared__ PackMeta sm[kStageMax];
     const int64_t n_work = n_tile * n_rg;
+    bool bad = false;
     for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
         int64_t jt;
         if (n_work <= int64_t(UINT32_MAX)) jt = int64_t(uint32_t(w) / uint32_t(n_rg));  // 32-bit divide
@@ -194,6 +219,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
                     for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
                     v[u] = pack8(h);
                 }
+                if constexpr (CHECK) bad |= out_of_range8<DT>(v[u], limit);
             }
 #pragma unroll
             for (int u = 0; u < kPackRows; ++u) {
@@ -217,12 +243,16 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
             if (x < b_base || x >= b_base + b_stride) continue;
             const int t0 = staged_search(sm, int(cnt), x);
             for (int64_t k = k0; k < kend; ++k)
-                pack_chunk_staged(sm, int(cnt), t0, k, x, packed + k * b_stride + (x - b_base));
+                pack_chunk_staged<DT, CHECK>(sm, int(cnt), t0, k, x, packed + k * b_stride + (x - b_base), limit, bad);
             continue;
         }
         if (x < b_base || x >= b_base + b_stride) continue;
         const int64_t i = param_of_column(P, x);
-        for (int64_t k = k0; k < kend; ++k) pack_chunk_generic(P, i, k, x, grads, packed + k * b_stride + (x - b_base));
+        for (int64_t k = k0; k < kend; ++k)
+            pack_chunk_generic<DT, CHECK>(P, i, k, x, grads, packed + k * b_stride + (x - b_base), limit, bad);
+    }
+    if constexpr (CHECK) {
+        if (bad) atomicOr(flag, 1);
     }
 }
 
@@ -413,23 +443,44 @@ using namespace zs;
 
 static const int64_t* bucket_row(const zero_plan* plan, int64_t b) { return plan->h_bucket + b * kBucketFields; }
 
-extern "C" zero_status zero_pack_bucket(const zero_plan* plan, int64_t b, const void* const* d_grad_ptrs, void* d_packed,
-                                        void* stream) {
+static zero_status pack_common(const zero_plan* plan, int64_t b, const void* const* d_grad_ptrs, void* d_packed,
+                               int32_t* d_flag, bool check, void* stream, const char* who) {
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
-    if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "zero_pack_bucket: bucket %lld out of range", (long long)b);
-    if (!d_grad_ptrs || !d_packed) return fail(ZERO_EINVAL, "zero_pack_bucket: NULL pointer");
-    if (!host_aligned16(d_packed)) return fail(ZERO_EINVAL, "zero_pack_bucket: packed buffer not 16-byte aligned");
+    if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "%s: bucket %lld out of range", who, (long long)b);
+    if (!d_grad_ptrs || !d_packed || (check && !d_flag)) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
+    if (!host_aligned16(d_packed)) return fail(ZERO_EINVAL, "%s: packed buffer not 16-byte aligned", who);
     const int64_t* br = bucket_row(plan, b);
     const int64_t base = br[BF_BASE], stride = br[BF_STRIDE];
     if (stride == 0) return ZERO_OK;
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + stride + kTileCols - 1) >> kTileShift) - tile0;
     const int64_t n_rg = (plan->nd + kPackRows - 1) / kPackRows;
-    pack_kernel<<<grid_for(n_tile * n_rg), kBlock, 0, (hipStream_t)stream>>>(
-        plan->dev, base, stride, tile0, n_tile, n_rg, reinterpret_cast<const uint16_t* const*>(d_grad_ptrs),
-        static_cast<uint16_t*>(d_packed));
-    return check_launch("zero_pack_bucket");
+    const int g = grid_for(n_tile * n_rg);
+    hipStream_t s = (hipStream_t)stream;
+    const uint16_t* const* grads = reinterpret_cast<const uint16_t* const*>(d_grad_ptrs);
+    uint16_t* packed = static_cast<uint16_t*>(d_packed);
+    const float limit = ldexpf(1.0f, 126) / float(plan->nd);
+    if (!check)
+        pack_kernel<0, false><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed, limit,
+                                                   nullptr);
+    else if (plan->dtype == ZERO_BF16)
+        pack_kernel<ZERO_BF16, true><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed,
+                                                          limit, d_flag);
+    else
+        pack_kernel<ZERO_FP16, true><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed,
+                                                          limit, d_flag);
+    return check_launch(who);
+}
+
+extern "C" zero_status zero_pack_bucket(const zero_plan* plan, int64_t b, const void* const* d_grad_ptrs, void* d_packed,
+                                        void* stream) {
+    return pack_common(plan, b, d_grad_ptrs, d_packed, nullptr, false, stream, "zero_pack_bucket");
+}
+
+extern "C" zero_status zero_pack_bucket_check(const zero_plan* plan, int64_t b, const void* const* d_grad_ptrs,
+                                              void* d_packed, int32_t* d_flag, void* stream) {
+    return pack_common(plan, b, d_grad_ptrs, d_packed, d_flag, true, stream, "zero_pack_bucket_check");
 }
 
 extern "C" zero_status zero_unpack(const zero_plan* plan, int64_t b, const void* d_gathered, void* const* d_param_ptrs,

@@ -13,29 +13,6 @@
 
 namespace zs {
 
-constexpr int kAhead = 8;
-
-// Bit t of the result is set when column x + t belongs to a live parameter.
-__device__ __forceinline__ unsigned live_mask8(const DevPlan& P, const uint8_t* __restrict__ live, int64_t x,
-                                               int64_t i) {
-    if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) return live[i] ? 0xffu : 0u;
-    unsigned m = 0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int64_t xt = x + t;
-        while (i < P.n && P.end[i] <= xt) ++i;
-        if (i < P.n && P.off[i] <= xt && live[i]) m |= 1u << t;
-    }
-    return m;
-}
-
-__device__ __forceinline__ void flag_if_bad(const float (&v)[8], unsigned mask, int32_t* flag) {
-    bool bad = false;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) bad |= ((mask >> t) & 1u) && non_finite(v[t]);
-    if (bad) atomicOr(flag, 1);
-}
-
 #ifndef ZS_REDUCE_TILES
 #define ZS_REDUCE_TILES 1
 #endif
@@ -45,19 +22,8 @@ template <int DT>
 __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, int64_t c, unsigned mask,
                                              const uint16_t* __restrict__ rows, int64_t row_stride,
                                              float* __restrict__ g32, int32_t* __restrict__ flag) {
-    const int64_t nd = P.nd;
-    const uint16_t* src = rows + c;
     float acc[8];
-    accumulate8<DT, true>(acc, load16(src));
-    int64_t k = 1;
-    for (; k + kAhead <= nd; k += kAhead) {
-        uint4 v[kAhead];
-#pragma unroll
-        for (int u = 0; u < kAhead; ++u) v[u] = load16(src + (k + u) * row_stride);
-#pragma unroll
-        for (int u = 0; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
-    }
-    for (; k < nd; ++k) accumulate8<DT, false>(acc, load16(src + k * row_stride));
+    reduce_rows8<DT>(rows + c, P.nd, row_stride, acc);
     float* dst = g32 + x;
     if (mask == 0xffu) {
         store4f(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));

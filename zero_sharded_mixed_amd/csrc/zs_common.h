@@ -189,11 +189,59 @@ __device__ __forceinline__ uint16_t from_f32(float f) {
         if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t(((u >> 16) & 0x8000u) | 0x7fc0u);
         return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
     } else {
+        // The empty asm pins f as a stored fp32 value: without it the compiler folds the
+        // conversion into the producing fma (a mixed-precision fma rounding the exact result
+        // straight to fp16), which differs from rounding the fp32 master when that value lies
+        // on an fp16 tie.
+        asm volatile("" : "+v"(f));
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
     }
 }
 
 __device__ __forceinline__ bool non_finite(float f) { return (__float_as_uint(f) & 0x7f800000u) == 0x7f800000u; }
+
+// ------------------------------------------------------------------ the Nd-way reduce --
+// Eight columns of the rank rows: acc = f32(row_0), then acc = acc + f32(row_k) for
+// k = 1..nd-1 (one fp32 round-to-nearest-even addition each, in this order).  Loads of the
+// next kAhead rows are issued ahead of their adds.
+constexpr int kAhead = 8;
+template <int DT>
+__device__ __forceinline__ void reduce_rows8(const uint16_t* __restrict__ src, int64_t nd, int64_t row_stride,
+                                             float (&acc)[8]) {
+    accumulate8<DT, true>(acc, load16(src));
+    int64_t k = 1;
+    for (; k + kAhead <= nd; k += kAhead) {
+        uint4 v[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) v[u] = load16(src + (k + u) * row_stride);
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
+    }
+    for (; k < nd; ++k) accumulate8<DT, false>(acc, load16(src + k * row_stride));
+}
+
+// Bit t of the result is set when column x + t belongs to a live parameter (i is the first
+// parameter with end > x).
+__device__ __forceinline__ unsigned live_mask8(const DevPlan& P, const uint8_t* __restrict__ live, int64_t x,
+                                               int64_t i) {
+    if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) return live[i] ? 0xffu : 0u;
+    unsigned m = 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int64_t xt = x + t;
+        while (i < P.n && P.end[i] <= xt) ++i;
+        if (i < P.n && P.off[i] <= xt && live[i]) m |= 1u << t;
+    }
+    return m;
+}
+
+// OR 1 into *flag if a masked value is inf or NaN (one atomic, only when found).
+__device__ __forceinline__ void flag_if_bad(const float (&v)[8], unsigned mask, int32_t* flag) {
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) bad |= ((mask >> t) & 1u) && non_finite(v[t]);
+    if (bad) atomicOr(flag, 1);
+}
 
 }  // namespace zs
 

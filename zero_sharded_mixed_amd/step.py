@@ -1,5 +1,5 @@
 """One rank's shard step, driven through the C ABI: pack -> reduce (+ overflow flag) -> Adam
--> unpack, the order of the ZeRO-1 sequence on the briefia.fr page ("ZeRO-1 : Partitionnement
+-> unpack (or pack with the input check -> fused reduce + Adam -> unpack), the order of the ZeRO-1 sequence on the briefia.fr page ("ZeRO-1 : Partitionnement
 des états de l'optimiseur": gradients synchronised, own partition stepped, parameters
 all-gathered) with the ZeRO-2 reduce-scatter of the ColossalAI "low level zero" issue (BWD).
 
@@ -53,10 +53,15 @@ class ShardStep:
     def init_master(self, src_ptrs: torch.Tensor, src_dtype: int = 0, stream=None) -> None:
         B.zero_shard_init(self.plan, src_ptrs, src_dtype, self.p32, stream)
 
-    def pack(self, grad_ptrs: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> None:
+    def pack(self, grad_ptrs: torch.Tensor, out: Optional[torch.Tensor] = None, check: bool = False,
+             stream=None) -> None:
+        """check=True: also OR this rank's input verdict into self.flag (the fused path's check)."""
         out = self.packed if out is None else out
         for b in range(len(self.buckets)):
-            B.zero_pack_bucket(self.plan, b, grad_ptrs, self.block(out, b), stream)
+            if check:
+                B.zero_pack_bucket_check(self.plan, b, grad_ptrs, self.block(out, b), self.flag, stream)
+            else:
+                B.zero_pack_bucket(self.plan, b, grad_ptrs, self.block(out, b), stream)
 
     def reduce(self, rows_of: Callable[[int], tuple], fused_check: bool = True, stream=None) -> None:
         """rows_of(b) -> (tensor starting at row 0 of bucket b, row stride in elements)."""
@@ -72,6 +77,17 @@ class ShardStep:
              stream=None) -> None:
         B.zero_adam_step(self.plan, self.g32, self.p32, self.m, self.v, self.live, self.steps, lr, beta1, beta2,
                          eps, grad_scale, self.flag if use_flag else None, self.arena, stream)
+
+    def reduce_adam(self, rows_of: Callable[[int], tuple], lr: float, beta1: float, beta2: float, eps: float,
+                    grad_scale: float, use_flag: bool = True, stream=None) -> None:
+        """The fused path after pack(check=True): step sizes once, then per bucket the sum of its
+        rows goes straight into the Adam update (self.g32 is not written)."""
+        flag = self.flag if use_flag else None
+        B.zero_adam_prepare(self.plan, self.live, self.steps, lr, beta1, beta2, eps, grad_scale, flag, stream)
+        for b in range(len(self.buckets)):
+            rows, stride = rows_of(b)
+            B.zero_reduce_adam_bucket(self.plan, b, rows, stride, self.live, self.p32, self.m, self.v, flag,
+                                      self.arena, stream)
 
     def unpack(self, param_ptrs: torch.Tensor, src: Optional[torch.Tensor] = None, stream=None) -> None:
         src = self.arena if src is None else src
