@@ -331,14 +331,17 @@ def cpu_baseline(w, max_elems: int):
 
 # ------------------------------------------------------------------- profile summaries --
 
-KERNEL_KEYS = (("adam_prepare_kernel", "adam_prepare"), ("unpack_kernel", "unpack"), ("pack_kernel", "pack"),
-               ("reduce_kernel", "reduce"), ("adam_kernel", "adam"), ("overflow_kernel", "overflow"),
-               ("shard_init_kernel", "shard_init"))
+KERNEL_KEYS = (("adam_prepare_kernel", "adam_prepare"), ("reduce_adam_kernel", "reduce_adam"),
+               ("unpack_kernel", "unpack"), ("pack_kernel", "pack"), ("reduce_kernel", "reduce"),
+               ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"))
+SHORT_NAMES = tuple(s for _, s in KERNEL_KEYS) + ("pack_check",)
 
 
 def _short(name: str) -> str:
     for key, short in KERNEL_KEYS:
         if key in name:
+            if short == "pack" and ("true>" in name or "Lb1E" in name):
+                return "pack_check"  # the pack with the input check (fused path)
             return short
     return name[:60]
 
@@ -364,7 +367,7 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
     stats = rows("trace/**/*kernel_stats.csv")
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         name = _short(r["Name"])
-        if name not in dict(KERNEL_KEYS).values() and float(r["Percentage"]) < 1.0:
+        if name not in SHORT_NAMES and float(r["Percentage"]) < 1.0:
             continue
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
@@ -392,7 +395,7 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
     src_hash = kernel_source_hash()
     for kname, vals in counters["FETCH_SIZE"].items():
         short = _short(kname)
-        if short not in dict(KERNEL_KEYS).values():
+        if short not in SHORT_NAMES:
             continue
         wv = counters["WRITE_SIZE"].get(kname, [0.0])
         fk, wk = sum(vals) / len(vals), sum(wv) / len(wv)
@@ -467,6 +470,12 @@ def main():
              "GBs": round(fz["bytes"] / (fz["ms"] * 1e-3) / 1e9, 1), "step_bytes": fz["bytes"],
              "elem_per_s": round(ab["shard_live"] / (fz["ms"] * 1e-3), 1), "overflow_flag": fz["flag"],
              "kernels": fz["kernels"]}
+    fk = fz["kernels"]["reduce_adam"]
+    fused["roofline"] = {"bound": "hbm", "kernel": "reduce_adam", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "achieved": fk["GBs"], "frac": fk["frac"],
+                         "traffic": measured_traffic("reduce_adam", WORKLOAD_IDS[args.config]),
+                         "bytes_per_launch": fk["bytes"] // fk["launches"],
+                         "avg_launch_ms": round(fk["ms"] / fk["launches"], 4)}
     dom = max(kernels, key=lambda p: kernels[p]["ms"])
     workload = WORKLOAD_IDS[args.config]
     traffic = measured_traffic(dom, workload)
