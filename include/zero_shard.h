@@ -121,17 +121,40 @@ typedef struct zero_plan_summary {
     int32_t device;         /* HIP device the plan lives on                              */
 } zero_plan_summary;
 
+/* Dynamic loss scaler, kept in device memory so that a step never waits for the host.  The
+ * pages do not treat loss scaling; this is the usual dynamic rule for 16-bit gradients: after
+ * a step whose overflow flag is set, scale = max(scale * backoff_factor, min_scale) and the
+ * step is counted in `overflows`; after growth_interval consecutive clean steps, scale =
+ * min(scale * growth_factor, max_scale) (fp32 products, round to nearest even).  The caller
+ * multiplies its loss by `scale` before the backward pass (reading it on the device) and
+ * passes the scaler to the Adam step through zero_adam_hparams.loss_scaler.  The caller owns
+ * the memory: sizeof(zero_loss_scaler) bytes, 4-byte aligned. */
+typedef struct zero_loss_scaler {
+    float scale;              /* the loss scale the current step's gradients carry       */
+    int32_t good_steps;       /* clean steps since the scale last changed                 */
+    int32_t growth_interval;  /* clean steps before the scale grows (>= 1)                */
+    float growth_factor;      /* >= 1                                                     */
+    float backoff_factor;     /* in (0, 1]                                                */
+    float min_scale;          /* 0 < min_scale <= scale <= max_scale, all finite          */
+    float max_scale;
+    int32_t overflows;        /* steps skipped so far                                     */
+} zero_loss_scaler;
+
 /* Adam hyperparameters.  The pages name Adam's momentum and variance as the optimizer
  * state [ZP model states; FR Problème de mémoire dans DDP] but give no update rule; the
  * step is textbook bias-corrected Adam without weight decay.  grad_scale multiplies the
  * reduced gradient before use: 1 / (Nd * loss_scale) turns the rank sum into the mean
- * of unscaled gradients. */
+ * of unscaled gradients.  With a dynamic loss scale, loss_scaler points to the device
+ * zero_loss_scaler and the multiplier is grad_scale / loss_scaler->scale (then grad_scale is
+ * 1 / Nd), formed in double on the device when the step runs and rounded to fp32 once;
+ * NULL = a static scale folded into grad_scale. */
 typedef struct zero_adam_hparams {
     double lr;
     double beta1;
     double beta2;
     double eps;
     double grad_scale;
+    const zero_loss_scaler* loss_scaler;  /* device pointer or NULL */
 } zero_adam_hparams;
 
 /* ---------------------------------------------------------------- plan ---------- */
@@ -215,7 +238,7 @@ zero_status zero_overflow_check(const zero_plan* plan, const float* d_g32, const
  * If d_flag is not NULL and *d_flag != 0 the whole step is skipped: nothing is written
  * and step counts stay.  Otherwise, for every live parameter i: d_steps[i] += 1,
  * t = d_steps[i], and for every element e of its slice (fp32 arithmetic):
- *     g = g32[e] * grad_scale
+ *     g = g32[e] * grad_scale        (grad_scale / loss_scaler->scale with a dynamic scaler)
  *     m = beta1*m + (1-beta1)*g ;  v = beta2*v + (1-beta2)*g*g
  *     p32 -= (lr / (1-beta1^t)) * m / (sqrt(v) / sqrt(1-beta2^t) + eps)
  *     arena[Nd*O_b + r*L_b + (e - O_b)] = round_to_nearest_even_16(p32)
@@ -225,8 +248,8 @@ zero_status zero_overflow_check(const zero_plan* plan, const float* d_g32, const
  *   d_live                   device uint8[n_params];  d_steps device int32[n_params]
  *   hp                       host pointer, read during the call
  *   d_arena                  device 16-bit [Nd * shard_numel], 16-byte aligned
- * Errors: ZERO_EINVAL for NULL/misaligned pointers or hyperparameters that are not finite
- * (lr, eps, grad_scale) or betas outside [0, 1). */
+ * Errors: ZERO_EINVAL for NULL/misaligned pointers (hp->loss_scaler 4-byte aligned if set) or
+ * hyperparameters that are not finite (lr, eps, grad_scale) or betas outside [0, 1). */
 zero_status zero_adam_step(const zero_plan* plan, const float* d_g32, float* d_p32, float* d_m, float* d_v,
                            const uint8_t* d_live, int32_t* d_steps, const zero_adam_hparams* hp,
                            const int32_t* d_flag, void* d_arena, void* stream);
@@ -299,6 +322,20 @@ zero_status zero_adam_prepare(const zero_plan* plan, const uint8_t* d_live, int3
 zero_status zero_reduce_adam_bucket(const zero_plan* plan, int64_t b, const void* d_rows, int64_t row_stride,
                                     const uint8_t* d_live, float* d_p32, float* d_m, float* d_v,
                                     const int32_t* d_flag, void* d_arena, void* stream);
+
+/* ------------------------------------------------------- dynamic loss scaling ------ */
+
+/* Write the host configuration *cfg (every field, good_steps and overflows included) to the
+ * device scaler d_scaler, in stream order.  *cfg is read during the call.
+ * Errors: ZERO_EINVAL for NULL or misaligned pointers, or a configuration outside the
+ * ranges stated in zero_loss_scaler. */
+zero_status zero_loss_scaler_init(const zero_loss_scaler* cfg, zero_loss_scaler* d_scaler, void* stream);
+
+/* After a step: apply the rule of zero_loss_scaler to d_scaler from the step's overflow flag
+ * *d_flag (read on the device; the flag is not changed).  Call once per step, after the Adam
+ * launches that read the scale, before the flag is cleared for the next step.
+ * Errors: ZERO_EINVAL for NULL or misaligned pointers. */
+zero_status zero_loss_scaler_update(const int32_t* d_flag, zero_loss_scaler* d_scaler, void* stream);
 
 /* Thread-local text of the last error ("" if none). */
 const char* zero_last_error(void);

@@ -63,6 +63,8 @@ def lib():
         L.oracle_reduce_bucket.restype = None
         L.oracle_reduce_bucket.argtypes = [vp, vp, i64, i64, vp, i64, i32, vp, vp]
         L.oracle_overflow.restype = i32
+        L.oracle_loss_scaler_update.restype = None
+        L.oracle_loss_scaler_update.argtypes = [vp, i32]
         L.oracle_input_check.restype = i32
         L.oracle_input_check.argtypes = [vp, vp, i64, i64, vp, i32]
         L.oracle_overflow.argtypes = [vp, i64, vp, vp]
@@ -168,6 +170,21 @@ def input_check(pl: Plan, b: int, grads, dtype: int) -> int:
     keep = [None if g is None else np.ascontiguousarray(g, dtype=np.uint16) for g in grads]
     table = _ptr_table(keep)
     return int(lib().oracle_input_check(_ptr(pl.params), _ptr(pl.buckets), pl.nd, b, _ptr(table), dtype))
+
+
+class Scaler(ctypes.Structure):
+    """The oracle's loss-scaler state (its own definition of the fields)."""
+    _fields_ = [("scale", ctypes.c_float), ("good_steps", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
+                ("growth_factor", ctypes.c_float), ("backoff_factor", ctypes.c_float), ("min_scale", ctypes.c_float),
+                ("max_scale", ctypes.c_float), ("overflows", ctypes.c_int32)]
+
+    def as_tuple(self):
+        return tuple(getattr(self, f) for f, _ in self._fields_)
+
+
+def loss_scaler_update(s: Scaler, flag: int) -> None:
+    """One step of the dynamic loss-scaling rule, in place."""
+    lib().oracle_loss_scaler_update(ctypes.byref(s), int(flag))
 
 
 @dataclass

@@ -341,6 +341,42 @@ void oracle_adam(const int64_t* params, const int64_t* buckets, int64_t n, int64
     }
 }
 
+/* ------------------------------------------------------ dynamic loss scaling ------ */
+/*
+ * Not on the pages (a reading: the usual dynamic rule for 16-bit gradients).  State: the
+ * current scale, the count of clean steps since it last changed, and the steps skipped.  A
+ * step with the overflow flag set multiplies the scale by the back-off factor (not below the
+ * minimum) and restarts the count; a clean step adds one to the count, and when the count
+ * reaches the growth interval the scale is multiplied by the growth factor (not above the
+ * maximum) and the count restarts.  Products in binary32.
+ */
+typedef struct {
+    float scale;
+    int32_t good_steps;
+    int32_t growth_interval;
+    float growth_factor;
+    float backoff_factor;
+    float min_scale;
+    float max_scale;
+    int32_t overflows;
+} oracle_scaler;
+
+void oracle_loss_scaler_update(oracle_scaler* s, int flag) {
+    if (flag) {
+        float backed = s->scale * s->backoff_factor;
+        s->scale = (backed < s->min_scale) ? s->min_scale : backed;
+        s->good_steps = 0;
+        s->overflows += 1;
+        return;
+    }
+    s->good_steps += 1;
+    if (s->good_steps == s->growth_interval) {
+        float grown = s->scale * s->growth_factor;
+        s->scale = (grown > s->max_scale) ? s->max_scale : grown;
+        s->good_steps = 0;
+    }
+}
+
 /* ---------------------------------------------------------------- unpack (O6) ------ */
 /*
  * [Z3]: after the ZeRO-1/2 all-gather every rank holds the full updated parameters.

@@ -87,9 +87,54 @@ def test_hot_calls_reject_null_plan(L):
     assert L.zero_adam_prepare(None, vp(16), vp(16), ctypes.byref(hp), None, None) == B.ZERO_EINVAL
     assert L.zero_reduce_adam_bucket(None, 0, vp(16), 8, vp(16), vp(16), vp(16), vp(16), None, vp(16),
                                      None) == B.ZERO_EINVAL
+    cfg = B.zero_loss_scaler(2.0 ** 16, 0, 100, 2.0, 0.5, 1.0, 2.0 ** 24, 0)
+    assert L.zero_loss_scaler_init(None, vp(16), None) == B.ZERO_EINVAL
+    assert L.zero_loss_scaler_init(ctypes.byref(cfg), None, None) == B.ZERO_EINVAL
+    assert L.zero_loss_scaler_init(ctypes.byref(cfg), vp(18), None) == B.ZERO_EINVAL  # misaligned
+    assert L.zero_loss_scaler_update(None, vp(16), None) == B.ZERO_EINVAL
+    assert L.zero_loss_scaler_update(vp(16), None, None) == B.ZERO_EINVAL
     s = B.zero_plan_summary()
     assert L.zero_plan_get_summary(None, ctypes.byref(s)) == B.ZERO_EINVAL
     L.zero_plan_destroy(None)  # no-op
+
+
+@pytest.mark.parametrize("bad", [dict(scale=0.0), dict(scale=float("inf")), dict(scale=float("nan")),
+                                 dict(min_scale=0.0, scale=1.0), dict(scale=0.5),  # below min_scale
+                                 dict(scale=2.0 ** 25),  # above max_scale
+                                 dict(growth_interval=0), dict(growth_factor=0.5), dict(backoff_factor=0.0),
+                                 dict(backoff_factor=1.5), dict(good_steps=100), dict(good_steps=-1),
+                                 dict(overflows=-1), dict(max_scale=float("inf"))])
+def test_loss_scaler_init_rejects(L, bad):
+    """Configuration checks happen on the host, before anything is launched."""
+    f = dict(scale=2.0 ** 16, good_steps=0, growth_interval=100, growth_factor=2.0, backoff_factor=0.5,
+             min_scale=1.0, max_scale=2.0 ** 24, overflows=0)
+    f.update(bad)
+    cfg = B.zero_loss_scaler(**f)
+    assert L.zero_loss_scaler_init(ctypes.byref(cfg), ctypes.c_void_p(16), None) == B.ZERO_EINVAL
+    assert Z.zero_last_error().startswith("zero_loss_scaler_init")
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structures have the C layout of include/zero_shard.h (gcc, host)."""
+    structs = {"zero_loss_scaler": B.zero_loss_scaler, "zero_adam_hparams": B.zero_adam_hparams,
+               "zero_param_info": B.zero_param_info, "zero_bucket_info": B.zero_bucket_info,
+               "zero_plan_summary": B.zero_plan_summary}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "zero_shard.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} %zu\\n", sizeof({name}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'printf("{name}.{fname} %zu\\n", offsetof({name}, {fname}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for fname, _ in cls._fields_:
+            assert int(got[f"{name}.{fname}"]) == getattr(cls, fname).offset, (name, fname)
 
 
 @pytest.mark.parametrize("psi,nd", [(7.5e9, 64), (1.5e9, 1), (1e12, 1024), (123456789.0, 3)])

@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_ENOMEM", -3: "ZERO_EH
 EXPORTS = ("zero_plan_create", "zero_plan_destroy", "zero_plan_get_summary", "zero_plan_param_info",
            "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes", "zero_pack_bucket",
            "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack", "zero_shard_init",
-           "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket", "zero_last_error")
+           "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket", "zero_loss_scaler_init",
+           "zero_loss_scaler_update", "zero_last_error")
 
 
 class ZeroError(RuntimeError):
@@ -49,8 +50,15 @@ class zero_plan_summary(ctypes.Structure):
                [("dtype", ctypes.c_int32), ("device", ctypes.c_int32)]
 
 
+class zero_loss_scaler(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float), ("good_steps", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
+                ("growth_factor", ctypes.c_float), ("backoff_factor", ctypes.c_float), ("min_scale", ctypes.c_float),
+                ("max_scale", ctypes.c_float), ("overflows", ctypes.c_int32)]
+
+
 class zero_adam_hparams(ctypes.Structure):
-    _fields_ = [(f, ctypes.c_double) for f in ("lr", "beta1", "beta2", "eps", "grad_scale")]
+    _fields_ = [(f, ctypes.c_double) for f in ("lr", "beta1", "beta2", "eps", "grad_scale")] + \
+               [("loss_scaler", ctypes.c_void_p)]
 
 
 _lib = None
@@ -83,6 +91,8 @@ def lib() -> ctypes.CDLL:
         "zero_pack_bucket_check": (i32, [vp, i64, vp, vp, vp, vp]),
         "zero_adam_prepare": (i32, [vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp]),
         "zero_reduce_adam_bucket": (i32, [vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
+        "zero_loss_scaler_init": (i32, [ctypes.POINTER(zero_loss_scaler), vp, vp]),
+        "zero_loss_scaler_update": (i32, [vp, vp, vp]),
         "zero_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
@@ -204,8 +214,10 @@ def zero_overflow_check(plan: Plan, g32: torch.Tensor, live: torch.Tensor, flag:
 
 def zero_adam_step(plan: Plan, g32: torch.Tensor, p32: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
                    live: torch.Tensor, steps: torch.Tensor, lr: float, beta1: float, beta2: float, eps: float,
-                   grad_scale: float, flag: Optional[torch.Tensor], arena: torch.Tensor, stream=None) -> None:
-    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale)
+                   grad_scale: float, flag: Optional[torch.Tensor], arena: torch.Tensor, stream=None,
+                   loss_scaler: Optional[torch.Tensor] = None) -> None:
+    """loss_scaler: device tensor holding a zero_loss_scaler (see LOSS_SCALER_BYTES), or None."""
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _ptr(loss_scaler))
     _check(lib().zero_adam_step(plan.handle, _ptr(g32), _ptr(p32), _ptr(m), _ptr(v), _ptr(live), _ptr(steps),
                                 ctypes.byref(hp), _ptr(flag), _ptr(arena), _stream(stream)))
 
@@ -224,8 +236,9 @@ def zero_pack_bucket_check(plan: Plan, b: int, grad_ptrs: torch.Tensor, packed: 
 
 
 def zero_adam_prepare(plan: Plan, live: torch.Tensor, steps: torch.Tensor, lr: float, beta1: float, beta2: float,
-                      eps: float, grad_scale: float, flag: Optional[torch.Tensor], stream=None) -> None:
-    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale)
+                      eps: float, grad_scale: float, flag: Optional[torch.Tensor], stream=None,
+                      loss_scaler: Optional[torch.Tensor] = None) -> None:
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _ptr(loss_scaler))
     _check(lib().zero_adam_prepare(plan.handle, _ptr(live), _ptr(steps), ctypes.byref(hp), _ptr(flag),
                                    _stream(stream)))
 
@@ -236,6 +249,26 @@ def zero_reduce_adam_bucket(plan: Plan, b: int, rows: torch.Tensor, row_stride: 
     """rows as in zero_reduce_shard; needs zero_adam_prepare earlier in the step on the same stream."""
     _check(lib().zero_reduce_adam_bucket(plan.handle, b, _ptr(rows), row_stride, _ptr(live), _ptr(p32), _ptr(m),
                                          _ptr(v), _ptr(flag), _ptr(arena), _stream(stream)))
+
+
+LOSS_SCALER_BYTES = ctypes.sizeof(zero_loss_scaler)
+
+
+def zero_loss_scaler_init(cfg: zero_loss_scaler, scaler: torch.Tensor, stream=None) -> None:
+    """scaler: device tensor of at least LOSS_SCALER_BYTES bytes (e.g. int32[8])."""
+    if scaler.numel() * scaler.element_size() < LOSS_SCALER_BYTES:
+        raise ValueError("loss scaler tensor too small")
+    _check(lib().zero_loss_scaler_init(ctypes.byref(cfg), _ptr(scaler), _stream(stream)))
+
+
+def zero_loss_scaler_update(flag: torch.Tensor, scaler: torch.Tensor, stream=None) -> None:
+    _check(lib().zero_loss_scaler_update(_ptr(flag), _ptr(scaler), _stream(stream)))
+
+
+def read_loss_scaler(scaler: torch.Tensor) -> zero_loss_scaler:
+    """Host copy of a device scaler (synchronises)."""
+    raw = scaler.detach().contiguous().view(torch.uint8)[:LOSS_SCALER_BYTES].cpu().numpy().tobytes()
+    return zero_loss_scaler.from_buffer_copy(raw)
 
 
 def zero_last_error() -> str:

@@ -12,7 +12,8 @@
 // Two launches on the caller's stream.  adam_prepare_kernel (one thread per parameter) reads
 // the overflow flag, bumps the step count of every live parameter and forms its step size
 // lr / (1 - beta1^t) and 1 / sqrt(1 - beta2^t) in double, rounded to fp32 once; it also forms
-// the fp32 hyperparameters (1 - beta computed in double, then rounded).  adam_kernel then
+// the fp32 hyperparameters (1 - beta computed in double, then rounded) and the gradient
+// multiplier (grad_scale, divided by the device loss scale when a dynamic scaler is given).  adam_kernel then
 // streams the shard, one block per span of kBlock * kAdamCols columns, reading g32, p32, m, v
 // and writing p32, m, v and the 16-bit parameters — 30 bytes per element.
 // Both kernels return at once when the flag is set, so a skipped step changes nothing.
@@ -24,7 +25,8 @@ namespace zs {
 
 __global__ void adam_prepare_kernel(DevPlan P, const uint8_t* __restrict__ live, int32_t* __restrict__ steps,
                                     const int32_t* __restrict__ flag, double lr, double beta1, double beta2, double eps,
-                                    double grad_scale, float2* __restrict__ scal, float* __restrict__ consts) {
+                                    double grad_scale, const zero_loss_scaler* __restrict__ scaler,
+                                    float2* __restrict__ scal, float* __restrict__ consts) {
     if (flag && *flag) return;
     const int64_t gid = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
     if (gid == 0) {
@@ -33,7 +35,8 @@ __global__ void adam_prepare_kernel(DevPlan P, const uint8_t* __restrict__ live,
         consts[AC_C1] = float(1.0 - beta1);
         consts[AC_C2] = float(1.0 - beta2);
         consts[AC_EPS] = float(eps);
-        consts[AC_GSCALE] = float(grad_scale);
+        // a dynamic loss scale divides out here, in double, before the one rounding to fp32
+        consts[AC_GSCALE] = float(scaler ? grad_scale / double(scaler->scale) : grad_scale);
     }
     for (int64_t i = gid; i < P.n; i += int64_t(gridDim.x) * blockDim.x) {
         if (!live[i]) continue;
@@ -168,8 +171,10 @@ zero_status launch_adam_prepare(const zero_plan* plan, const uint8_t* d_live, in
     if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->grad_scale) || !(hp->beta1 >= 0.0) ||
         !(hp->beta1 < 1.0) || !(hp->beta2 >= 0.0) || !(hp->beta2 < 1.0))
         return fail(ZERO_EINVAL, "%s: hyperparameters out of range", who);
+    if (reinterpret_cast<uintptr_t>(hp->loss_scaler) % alignof(zero_loss_scaler) != 0)
+        return fail(ZERO_EINVAL, "%s: loss scaler not 4-byte aligned", who);
     adam_prepare_kernel<<<grid_for((plan->n + 255) / 256, 1024), 256, 0, s>>>(
-        plan->dev, d_live, d_steps, d_flag, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->grad_scale,
+        plan->dev, d_live, d_steps, d_flag, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->grad_scale, hp->loss_scaler,
         reinterpret_cast<float2*>(plan->d_adam_scal), plan->d_adam_const);
     return check_launch(who);
 }

@@ -18,10 +18,12 @@ enum AdamConst { AC_BETA1, AC_BETA2, AC_C1, AC_C2, AC_EPS, AC_GSCALE, kAdamConst
 // One thread per parameter.  If the flag is set the step is skipped: nothing is written.
 // Otherwise every live parameter's step count advances and its step size lr / (1 - beta1^t)
 // and 1 / sqrt(1 - beta2^t) are formed in double and rounded to fp32 once; thread 0 also forms
-// the fp32 hyperparameters (1 - beta in double, then rounded).
+// the fp32 hyperparameters (1 - beta in double, then rounded) and the gradient multiplier
+// grad_scale (/ scaler->scale when a device loss scaler is given).
 __global__ void adam_prepare_kernel(DevPlan P, const uint8_t* __restrict__ live, int32_t* __restrict__ steps,
                                     const int32_t* __restrict__ flag, double lr, double beta1, double beta2, double eps,
-                                    double grad_scale, float2* __restrict__ scal, float* __restrict__ consts);
+                                    double grad_scale, const zero_loss_scaler* __restrict__ scaler,
+                                    float2* __restrict__ scal, float* __restrict__ consts);
 
 struct AdamK {
     float b1, b2, c1, c2, eps, gs;

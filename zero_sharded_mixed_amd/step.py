@@ -37,6 +37,19 @@ class ShardStep:
         # bucket b's [Nd][L_b] block starts at block_offset
         self.packed = torch.zeros(int(s.arena_numel), dtype=torch.int16, device=self.device)
         self.arena = torch.zeros(int(s.arena_numel), dtype=torch.int16, device=self.device)
+        self.scaler: Optional[torch.Tensor] = None  # device zero_loss_scaler, once enabled
+
+    def enable_loss_scaler(self, scale: float, growth_interval: int = 2000, growth_factor: float = 2.0,
+                           backoff_factor: float = 0.5, min_scale: float = 1.0, max_scale: float = 2.0 ** 24,
+                           stream=None) -> None:
+        """Dynamic loss scaling on the device; adam()/reduce_adam() then divide the gradient
+        multiplier by the current scale, and update_loss_scale() applies the rule after a step."""
+        self.scaler = torch.zeros(B.LOSS_SCALER_BYTES // 4, dtype=torch.int32, device=self.device)
+        cfg = B.zero_loss_scaler(scale, 0, growth_interval, growth_factor, backoff_factor, min_scale, max_scale, 0)
+        B.zero_loss_scaler_init(cfg, self.scaler, stream)
+
+    def update_loss_scale(self, stream=None) -> None:
+        B.zero_loss_scaler_update(self.flag, self.scaler, stream)
 
     # -- views ---------------------------------------------------------------------------
     def block(self, buf: torch.Tensor, b: int) -> torch.Tensor:
@@ -76,14 +89,15 @@ class ShardStep:
     def adam(self, lr: float, beta1: float, beta2: float, eps: float, grad_scale: float, use_flag: bool = True,
              stream=None) -> None:
         B.zero_adam_step(self.plan, self.g32, self.p32, self.m, self.v, self.live, self.steps, lr, beta1, beta2,
-                         eps, grad_scale, self.flag if use_flag else None, self.arena, stream)
+                         eps, grad_scale, self.flag if use_flag else None, self.arena, stream, loss_scaler=self.scaler)
 
     def reduce_adam(self, rows_of: Callable[[int], tuple], lr: float, beta1: float, beta2: float, eps: float,
                     grad_scale: float, use_flag: bool = True, stream=None) -> None:
         """The fused path after pack(check=True): step sizes once, then per bucket the sum of its
         rows goes straight into the Adam update (self.g32 is not written)."""
         flag = self.flag if use_flag else None
-        B.zero_adam_prepare(self.plan, self.live, self.steps, lr, beta1, beta2, eps, grad_scale, flag, stream)
+        B.zero_adam_prepare(self.plan, self.live, self.steps, lr, beta1, beta2, eps, grad_scale, flag, stream,
+                            loss_scaler=self.scaler)
         for b in range(len(self.buckets)):
             rows, stride = rows_of(b)
             B.zero_reduce_adam_bucket(self.plan, b, rows, stride, self.live, self.p32, self.m, self.v, flag,
