@@ -73,6 +73,49 @@ def expected_arena(pl: oracle.Plan, oracle_arena: np.ndarray, got_p32: np.ndarra
     return want
 
 
+def ordered16(h: np.ndarray) -> np.ndarray:
+    """Integers in the order of the 16-bit float values (sign-magnitude to two's complement)."""
+    h = h.astype(np.int64)
+    return np.where(h < 0x8000, h, -(h & 0x7FFF))
+
+
+def one_ulp_implied(p_ref: np.ndarray, dtype: int, rel: float = 1e-6, abs_: float = 1e-7) -> np.ndarray:
+    """Where |p - p_ref| <= abs_ + rel |p_ref| forces RNE16(p) within one 16-bit ulp of
+    RNE16(p_ref): the tolerance is at most half the smallest 16-bit ulp near p_ref (the ulp of
+    |p_ref| / 2), so the interval crosses at most one rounding boundary.  False only near zero,
+    where the absolute tolerance exceeds a 16-bit ulp."""
+    a = np.abs(p_ref.astype(np.float64))
+    mant, emin = (7, -126) if dtype == 1 else (10, -14)
+    e = np.floor(np.log2(np.maximum(a / 2, 2.0 ** -160)))
+    ulp = 2.0 ** (np.maximum(e, emin) - mant)
+    return abs_ + rel * a <= ulp / 2
+
+
+def assert_lp_within_ulp(got16: np.ndarray, want16: np.ndarray, p_ref: np.ndarray, dtype: int, what: str) -> None:
+    """16-bit parameters within one ulp of the oracle's wherever the p32 tolerance implies it."""
+    m = one_ulp_implied(p_ref, dtype)
+    d = np.abs(ordered16(got16) - ordered16(want16))
+    bad = m & (d > 1)
+    if bad.any():
+        i = np.flatnonzero(bad)[0]
+        raise AssertionError(f"{what}: {np.count_nonzero(bad)} beyond 1 ulp; first at {i}: got {got16[i]:#06x} "
+                             f"want {want16[i]:#06x} (p_ref {p_ref[i]!r})")
+
+
+def check_arena(pl: oracle.Plan, got_arena: np.ndarray, oracle_arena: np.ndarray, got_p32: np.ndarray,
+                oracle_p32: np.ndarray, ever: np.ndarray, dtype: int, what: str) -> None:
+    """The arena after Adam steps: bit-exact against the RNE of the kernel's own p32 where a
+    parameter has stepped and against the oracle elsewhere (expected_arena), and within one
+    ulp of the oracle's 16-bit parameters wherever the p32 tolerance implies it."""
+    assert np.array_equal(got_arena, expected_arena(pl, oracle_arena, got_p32, ever, dtype)), what
+    for b in range(pl.n_buckets):
+        O, L = int(pl.buckets[b, oracle.B_BASE]), int(pl.buckets[b, oracle.B_STRIDE])
+        at = pl.nd * O + pl.rank * L
+        sel = ever[O:O + L]
+        assert_lp_within_ulp(got_arena[at:at + L][sel], oracle_arena[at:at + L][sel], oracle_p32[O:O + L][sel], dtype,
+                             f"{what} bucket {b}")
+
+
 def ragged_numels(rng: np.random.Generator, n: int, nd: int, hi: int) -> list:
     """A ragged list that exercises every layout case: empty parameters, numel < nd, exact
     multiples of nd, primes, and log-uniform sizes up to hi."""

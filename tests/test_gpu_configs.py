@@ -17,8 +17,9 @@ import torch
 import oracle
 import workloads as W
 import zero_sharded_mixed_amd as Z
-from gpu_harness import (DEV, assert_close_f32, assert_same_f32, bits16, column_owner, expected_arena, gather_params,
-                         oracle_block, row_zero_mask, sample_columns, say, to_np16, to_np32)
+from gpu_harness import (DEV, assert_close_f32, assert_lp_within_ulp, assert_same_f32, bits16, check_arena,
+                         column_owner, gather_params, oracle_block, row_zero_mask, sample_columns, say, to_np16,
+                         to_np32)
 
 pytestmark = pytest.mark.gpu
 P_OFF, P_S, P_NUMEL, P_COL, P_BUCKET, P_START = (oracle.P_OFFSET, oracle.P_SHARD, oracle.P_NUMEL, oracle.P_COL,
@@ -106,7 +107,7 @@ def test_mlp_model_every_element_three_steps():
         assert_close_f32(to_np32(st.v), v, f"v step {step}")
         for i in np.flatnonzero(live):
             ever[pl.params[i, P_OFF]:pl.params[i, P_OFF] + pl.params[i, P_S]] = True
-        assert np.array_equal(to_np16(st.arena), expected_arena(pl, arena, to_np32(st.p32), ever, w.dtype)), step
+        check_arena(pl, to_np16(st.arena), arena, to_np32(st.p32), p32, ever, w.dtype, f"arena {step}")
         for i in (2, 3):  # the dropped layer: p32 / m / v bit-identical
             o, s_ = pl.params[i, P_OFF], pl.params[i, P_S]
             for old, t in zip(before, (st.p32, st.m, st.v)):
@@ -272,6 +273,8 @@ def run_fullsize(config, max_steps=None, n_samples=20000):
         # the 16-bit parameter is the RNE of the kernel's own p32 (checked against the oracle above)
         got_p = to_np32(st.p32[cols_dev])
         assert np.array_equal(got_lp[ever_live], oracle.from_f32(got_p[ever_live], w.dtype)), f"lp step {step}"
+        assert_lp_within_ulp(got_lp[ever_live], oracle.from_f32(o_p32[ever_live], w.dtype), o_p32[ever_live], w.dtype,
+                             f"lp step {step}")
         assert np.array_equal(got_lp[~ever_live], o_lp_before[~ever_live]), f"untouched lp step {step}"
         del own, own_ptrs
         if w.emulation != "full":

@@ -12,8 +12,8 @@ import torch
 import oracle
 import workloads as W
 import zero_sharded_mixed_amd as Z
-from gpu_harness import (DEV, assert_close_f32, bits16, ragged_numels, column_owner, expected_arena,
-                         gather_params, random_bits, row_zero_mask, sample_columns, say, to_dev16, to_np16, to_np32)
+from gpu_harness import (DEV, assert_close_f32, bits16, check_arena, column_owner, gather_params, ragged_numels,
+                         random_bits, row_zero_mask, sample_columns, say, to_dev16, to_np16, to_np32)
 
 pytestmark = pytest.mark.gpu
 BF16, FP16 = Z.ZERO_BF16, Z.ZERO_FP16
@@ -221,7 +221,7 @@ def test_fused_matches_unfused_and_oracle(case, dtype):
             for i in np.flatnonzero(live):
                 ever[pl.params[i, P_OFF]:pl.params[i, P_OFF] + pl.params[i, P_S]] = True
         got_arena = to_np16(F.arena)
-        assert np.array_equal(got_arena, expected_arena(pl, arena, to_np32(F.p32), ever, dtype)), f"arena {step}"
+        check_arena(pl, got_arena, arena, to_np32(F.p32), p32, ever, dtype, f"arena {step}")
 
 
 def test_fused_without_flag_steps_regardless():

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import zero_sharded_mixed_amd as Z
-from gpu_harness import (DEV, assert_close_f32, assert_same_f32, expected_arena, oracle_block, placed_views,
+from gpu_harness import (DEV, assert_close_f32, assert_same_f32, check_arena, oracle_block, placed_views,
                          ragged_numels, random_bits, say, to_dev16, to_np16, to_np32)
 
 pytestmark = pytest.mark.gpu
@@ -243,7 +243,7 @@ def test_adam_steps(case, dtype):
                 keep[o:o + s] = False
         ever |= ~keep
         got_arena = to_np16(st.arena)
-        assert np.array_equal(got_arena, expected_arena(pl, arena, to_np32(st.p32), ever, dtype)), f"arena {step}"
+        check_arena(pl, got_arena, arena, to_np32(st.p32), p32, ever, dtype, f"arena {step}")
         for name, old, t in zip("pmv", before, (st.p32, st.m, st.v)):
             assert np.array_equal(old[keep].view(np.uint32), to_np32(t)[keep].view(np.uint32)), name
 

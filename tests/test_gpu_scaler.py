@@ -7,8 +7,8 @@ import torch
 
 import oracle
 import zero_sharded_mixed_amd as Z
-from gpu_harness import DEV, assert_close_f32, expected_arena, random_bits, ragged_numels, say, to_dev16, to_np16, \
-    to_np32
+from gpu_harness import (DEV, assert_close_f32, check_arena, ragged_numels, random_bits, say, to_dev16, to_np16,
+                         to_np32)
 
 pytestmark = pytest.mark.gpu
 FP16 = Z.ZERO_FP16
@@ -110,7 +110,7 @@ def test_adam_with_device_scale_both_paths():
         if not overflow:
             for i in np.flatnonzero(live):
                 ever[pl.params[i, oracle.P_OFFSET]:pl.params[i, oracle.P_OFFSET] + pl.params[i, oracle.P_SHARD]] = True
-        assert np.array_equal(to_np16(A.arena), expected_arena(pl, arena, to_np32(A.p32), ever, FP16)), step
+        check_arena(pl, to_np16(A.arena), arena, to_np32(A.p32), p32, ever, FP16, f"arena {step}")
     assert o_s.scale == 2.0 ** 16 and o_s.overflows == 2  # grew at step 1, halved at 2 and 4, grew at 6
 
 

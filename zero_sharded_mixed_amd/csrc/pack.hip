@@ -251,9 +251,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
         for (int64_t k = k0; k < kend; ++k)
             pack_chunk_generic<DT, CHECK>(P, i, k, x, grads, packed + k * b_stride + (x - b_base), limit, bad);
     }
-    if constexpr (CHECK) {
-        if (bad) atomicOr(flag, 1);
-    }
+    if constexpr (CHECK) flag_wave(bad, flag);
 }
 
 // ----------------------------------------------------------------------------- unpack --

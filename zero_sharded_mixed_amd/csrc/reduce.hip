@@ -8,7 +8,8 @@
 // 16-byte boundaries), converts exactly to fp32 and adds in ascending rank order, seeded with
 // rank 0's value — the fixed order that makes the sums bit-reproducible.  Loads of the next
 // ranks are issued ahead of the adds (kAhead rows in flight) so HBM latency overlaps.
-// Columns of parameters without a gradient are skipped before any row is read.
+// Columns of parameters without a gradient are skipped before any row is read.  The overflow
+// flag is ORed once per wavefront (a ballot, then one atomic), only when a value is found.
 #include "zs_common.h"
 
 namespace zs {
@@ -21,7 +22,7 @@ constexpr int kReduceTiles = ZS_REDUCE_TILES;  // consecutive tiles per block (o
 template <int DT>
 __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, int64_t c, unsigned mask,
                                              const uint16_t* __restrict__ rows, int64_t row_stride,
-                                             float* __restrict__ g32, int32_t* __restrict__ flag) {
+                                             float* __restrict__ g32, bool& bad) {
     float acc[8];
     reduce_rows8<DT>(rows + c, P.nd, row_stride, acc);
     float* dst = g32 + x;
@@ -33,7 +34,7 @@ __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, int64_
         for (int t = 0; t < 8; ++t)
             if (mask & (1u << t)) gptr(dst)[t] = acc[t];
     }
-    if (flag) flag_if_bad(acc, mask, flag);
+    bad |= any_bad8(acc, mask);
 }
 
 template <int DT>
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_bas
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
     const int64_t n_groups = (n_tile + kReduceTiles - 1) / kReduceTiles;
+    bool bad = false;
     for (int64_t w = blockIdx.x; w < n_groups; w += gridDim.x) {
         const int64_t j = tile0 + w * kReduceTiles;
         const int64_t x0 = j << kTileShift;
@@ -60,13 +62,15 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_bas
             if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
             const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
             if (mask == 0) continue;
-            reduce_chunk<DT>(P, x, c, mask, rows, row_stride, g32, flag);
+            reduce_chunk<DT>(P, x, c, mask, rows, row_stride, g32, bad);
         }
     }
+    if (flag) flag_wave(bad, flag);
 }
 
 __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,
                                                           const uint8_t* __restrict__ live, int32_t* __restrict__ flag) {
+    bool bad = false;
     for (int64_t j = blockIdx.x; j < P.n_tiles; j += gridDim.x) {
         const int64_t x = (j << kTileShift) + int64_t(threadIdx.x) * kChunk;
         if (x >= P.shard_numel) continue;
@@ -75,8 +79,9 @@ __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float
         const float4 a = load4f(g32 + x);
         const float4 b = load4f(g32 + x + 4);
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        flag_if_bad(v, mask, flag);
+        bad |= any_bad8(v, mask);
     }
+    flag_wave(bad, flag);
 }
 
 }  // namespace zs

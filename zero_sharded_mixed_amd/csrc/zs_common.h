@@ -235,12 +235,20 @@ __device__ __forceinline__ unsigned live_mask8(const DevPlan& P, const uint8_t* 
     return m;
 }
 
-// OR 1 into *flag if a masked value is inf or NaN (one atomic, only when found).
-__device__ __forceinline__ void flag_if_bad(const float (&v)[8], unsigned mask, int32_t* flag) {
+// True if a masked value is inf or NaN.
+__device__ __forceinline__ bool any_bad8(const float (&v)[8], unsigned mask) {
     bool bad = false;
 #pragma unroll
     for (int t = 0; t < 8; ++t) bad |= ((mask >> t) & 1u) && non_finite(v[t]);
-    if (bad) atomicOr(flag, 1);
+    return bad;
+}
+
+// OR 1 into *flag when `bad` holds on any active lane of the wavefront: a ballot across the
+// lanes, then one atomic from the lowest lane that found a value (none when nothing was found).
+// Called once per thread after its loops, where the wavefront has reconverged.
+__device__ __forceinline__ void flag_wave(bool bad, int32_t* flag) {
+    const unsigned long long m = __ballot(bad);
+    if (m != 0ull && __lane_id() == unsigned(__builtin_ctzll(m))) atomicOr(flag, 1);
 }
 
 }  // namespace zs
