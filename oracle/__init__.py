@@ -55,7 +55,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
         L.oracle_plan.restype = i64
-        L.oracle_plan.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp]
+        L.oracle_plan.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
         L.oracle_pack_bucket.restype = None
         L.oracle_pack_bucket.argtypes = [vp, vp, i64, i64, vp, vp]
         L.oracle_reduce_column.restype = ctypes.c_float
@@ -121,13 +121,18 @@ class Plan:
         return range(int(first), int(first + count))
 
 
-def plan(numels, nd: int, rank: int, bucket_bytes: int) -> Plan:
+def plan(numels, nd: int, rank: int, bucket_bytes: int, groups=None) -> Plan:
+    """groups: one int32 id per parameter (a bucket never spans a change of id), or None."""
     numels = np.ascontiguousarray(numels, dtype=np.int64)
     n = numels.shape[0]
+    if groups is not None:
+        groups = np.ascontiguousarray(groups, dtype=np.int32)
+        assert groups.shape == (n,)
     params = np.zeros((max(n, 1), 9), dtype=np.int64)
     buckets = np.zeros((max(n, 1), 5), dtype=np.int64)
     shard_len = np.zeros(1, dtype=np.int64)
-    nb = lib().oracle_plan(_ptr(numels), n, nd, rank, bucket_bytes, _ptr(params), _ptr(buckets), _ptr(shard_len))
+    nb = lib().oracle_plan(_ptr(numels), None if groups is None else _ptr(groups), n, nd, rank, bucket_bytes,
+                           _ptr(params), _ptr(buckets), _ptr(shard_len))
     if nb < 0:
         raise ValueError("oracle_plan: invalid arguments")
     return Plan(params[:n].copy(), buckets[:nb].copy(), int(shard_len[0]), nd, rank)

@@ -71,11 +71,14 @@ int oracle_bucket_fields(void) { return ORB_NFIELDS; }
  * [LLZ INIT]: every parameter is split evenly over the ranks, rank r keeps row r.
  * [LLZ BWD]: gradients go into buckets; when full, each one is viewed as [Nd, -1] and the
  * rows of one rank are flattened together.
+ * [Z3]: ZeRO-3 gathers and frees the parameters one layer (unit) at a time; with groups (one
+ * id per parameter, NULL = a single group), a bucket also ends where the group id changes, so
+ * that every bucket lies inside one unit.
  * Returns the number of buckets, or -1 on an invalid argument.  params: n * ORP_NFIELDS,
  * buckets: n * ORB_NFIELDS (n is an upper bound on the bucket count).
  */
-int64_t oracle_plan(const int64_t* numels, int64_t n, int64_t nd, int64_t rank, int64_t bucket_bytes,
-                    int64_t* params, int64_t* buckets, int64_t* shard_len) {
+int64_t oracle_plan(const int64_t* numels, const int32_t* groups, int64_t n, int64_t nd, int64_t rank,
+                    int64_t bucket_bytes, int64_t* params, int64_t* buckets, int64_t* shard_len) {
     if (n < 1 || nd < 1 || rank < 0 || rank >= nd || bucket_bytes < 0) return -1;
     for (int64_t i = 0; i < n; i++) {
         if (numels[i] < 0) return -1;
@@ -100,7 +103,8 @@ int64_t oracle_plan(const int64_t* numels, int64_t n, int64_t nd, int64_t rank, 
     for (int64_t i = 0; i < n; i++) {
         int64_t padded = params[i * ORP_NFIELDS + ORP_PADDED];
         int open_nonempty = nb > 0 && buckets[(nb - 1) * ORB_NFIELDS + ORB_COUNT] > 0;
-        if (nb == 0 || (bucket_bytes > 0 && open_nonempty && fill + padded > capacity)) {
+        int new_group = groups != NULL && i > 0 && groups[i] != groups[i - 1];
+        if (nb == 0 || new_group || (bucket_bytes > 0 && open_nonempty && fill + padded > capacity)) {
             int64_t* bk = buckets + nb * ORB_NFIELDS;
             bk[ORB_FIRST] = i;
             bk[ORB_COUNT] = 0;

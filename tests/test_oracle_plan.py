@@ -150,3 +150,61 @@ def test_bucket_filled_exactly_stays_one_bucket():
     assert pl.n_buckets == 1
     pl = oracle.plan([10, 0, 2], 1, 0, 2 * 8)  # an oversize parameter is alone, even before an empty one
     assert list(pl.buckets[:, B_COUNT]) == [1, 2]
+
+
+# ------------------------------------------------------ grouped plans (ZeRO-3 units) --
+
+def _runs(groups):
+    """[start, end) of every maximal run of equal ids."""
+    out, a = [], 0
+    for i in range(1, len(groups) + 1):
+        if i == len(groups) or groups[i] != groups[i - 1]:
+            out.append((a, i))
+            a = i
+    return out
+
+
+@pytest.mark.parametrize("nd,cap", [(1, 0), (3, 2 * 500), (8, 2 * 4000), (8, 0), (64, 2 * 30000)])
+def test_grouped_plan_is_the_concatenation_of_per_group_plans(nd, cap):
+    """A grouped plan is the plans of each run of equal ids laid one after the other: buckets,
+    columns and every field the same, bucket indices and shard offsets shifted by what the
+    earlier runs hold (an independent restatement: each run planned on its own)."""
+    rng = np.random.default_rng(nd * 7 + cap)
+    for trial in range(6):
+        n = int(rng.integers(1, 60))
+        numels = rng.integers(0, 5000, size=n)
+        groups = np.cumsum(rng.random(n) < 0.25).astype(np.int32)
+        if trial == 5:
+            groups = (np.arange(n) // 3 % 2).astype(np.int32)  # ids that come back: runs, not sets
+        pl = oracle.plan(numels, nd, nd - 1, cap, groups)
+        bshift = pshift = 0
+        for a, e in _runs(groups):
+            sub = oracle.plan(numels[a:e], nd, nd - 1, cap)
+            got = pl.params[a:e].copy()
+            want = sub.params.copy()
+            want[:, P_BUCKET] += bshift
+            want[:, P_OFFSET] += pshift
+            assert np.array_equal(got, want), (trial, a, e)
+            gb = pl.buckets[bshift:bshift + sub.n_buckets].copy()
+            wb = sub.buckets.copy()
+            wb[:, B_FIRST] += a
+            wb[:, B_BASE] += pshift
+            assert np.array_equal(gb, wb), (trial, a, e)
+            bshift += sub.n_buckets
+            pshift += sub.shard_len
+        assert bshift == pl.n_buckets and pshift == pl.shard_len
+
+
+def test_grouped_plan_special_cases():
+    numels = [100, 7, 3000, 0, 45, 45]
+    # one group: the ungrouped plan
+    a = oracle.plan(numels, 8, 2, 2 * 1000)
+    b = oracle.plan(numels, 8, 2, 2 * 1000, np.zeros(6, np.int32))
+    assert np.array_equal(a.params, b.params) and np.array_equal(a.buckets, b.buckets)
+    # every parameter its own group: one bucket each, whatever the capacity
+    for cap in (0, 2, 10 ** 9):
+        c = oracle.plan(numels, 8, 2, cap, np.arange(6, dtype=np.int32))
+        assert c.n_buckets == 6 and list(c.buckets[:, B_COUNT]) == [1] * 6
+    # unbounded capacity: exactly the runs of equal ids
+    d = oracle.plan(numels, 8, 2, 0, np.array([5, 5, 1, 1, 1, 5], np.int32))
+    assert list(d.buckets[:, B_FIRST]) == [0, 2, 5] and list(d.buckets[:, B_COUNT]) == [2, 3, 1]
