@@ -175,6 +175,16 @@ typedef struct zero_adam_hparams {
 zero_status zero_plan_create(const int64_t* numels, int64_t n_params, int32_t nd, int32_t rank,
                              int64_t bucket_bytes, int32_t dtype, zero_plan** out);
 
+/* zero_plan_create with parameter groups [Z3: ZeRO-3 gathers, uses and frees the parameters
+ * one layer at a time]: groups[i] is parameter i's group id (any int32; host array), and a
+ * bucket is also closed before every parameter whose id differs from its predecessor's, so
+ * every bucket lies inside one run of equal ids; inside a run the capacity rule above holds.
+ * With one bucket per layer, a layer's gather is zero_unpack of its bucket and its
+ * reduce-scatter is zero_pack_bucket + zero_reduce_shard.  groups == NULL is zero_plan_create.
+ * Errors: as zero_plan_create. */
+zero_status zero_plan_create_grouped(const int64_t* numels, const int32_t* groups, int64_t n_params, int32_t nd,
+                                     int32_t rank, int64_t bucket_bytes, int32_t dtype, zero_plan** out);
+
 /* Free a plan (NULL is a no-op).  Call only after work using it has finished. */
 void zero_plan_destroy(zero_plan* plan);
 

@@ -68,6 +68,25 @@ def test_plan_create_rejects(L, kw, status):
     assert Z.zero_last_error().startswith("zero_plan_create")
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(numels=[]), B.ZERO_EINVAL),
+    (dict(numels=[5], nd=0), B.ZERO_EINVAL),
+    (dict(numels=[5, -1]), B.ZERO_EINVAL),
+    (dict(numels=[1 << 48]), B.ZERO_ERANGE),
+])
+def test_grouped_plan_create_rejects(L, kw, status):
+    """The grouped entry point validates exactly as zero_plan_create (before any device work)."""
+    numels = kw.pop("numels")
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*numels)
+    groups = (ctypes.c_int32 * max(len(numels), 1))(*range(len(numels)))
+    h = ctypes.c_void_p(123)
+    args = dict(nd=8, rank=0, bucket_bytes=0, dtype=1)
+    args.update(kw)
+    st = L.zero_plan_create_grouped(arr, groups, len(numels), args["nd"], args["rank"], args["bucket_bytes"],
+                                    args["dtype"], ctypes.byref(h))
+    assert st == status and h.value is None
+
+
 def test_plan_create_null_out(L):
     st, _ = _create(L, [5], out=False)
     assert st == B.ZERO_EINVAL

@@ -1,0 +1,120 @@
+"""ZeRO-3's per-layer parameter path on the GPU, through the C ABI: grouped plans (one bucket
+per layer) against the oracle's tables, and a whole ZeRO-3 step of a layered model — every
+layer gathered before use in the order of the llm-engineer "ZeRO-3" card (0 -> 1 -> 2 -> 1 -> 0
+for three layers), each gather checked bit for bit against the oracle's unpack, each layer's
+gradients reduce-scattered right after its backward, then Adam — against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_sharded_mixed_amd as Z
+from gpu_harness import (DEV, assert_close_f32, assert_same_f32, check_arena, oracle_block, random_bits, say,
+                         to_dev16, to_np16, to_np32)
+
+pytestmark = pytest.mark.gpu
+BF16, FP16 = Z.ZERO_BF16, Z.ZERO_FP16
+
+
+def layered_model(n_layers, d, vocab):
+    """Embedding, then blocks of [w1 (d x 4d), b1 (4d), w2 (4d x d), b2 (d), ln w (d), ln b (d)],
+    then a final norm; returns numels and the layer (group) of each parameter."""
+    numels, groups = [vocab * d], [0]
+    for layer in range(1, n_layers + 1):
+        for x in (d * 4 * d, 4 * d, 4 * d * d, d, d, d):
+            numels.append(x)
+            groups.append(layer)
+    numels += [d, d]
+    groups += [n_layers + 1, n_layers + 1]
+    return numels, groups
+
+
+@pytest.mark.parametrize("nd,cap,seed", [(8, 0, 1), (8, 2 * 20000, 2), (3, 2 * 5000, 3), (64, 0, 4)])
+def test_grouped_plan_tables(nd, cap, seed):
+    rng = np.random.default_rng(seed)
+    n = 150
+    numels = [int(x) for x in rng.integers(0, 50000, size=n)]
+    groups = np.cumsum(rng.random(n) < 0.2).astype(np.int32)
+    groups[100:120] = groups[99] + np.arange(20) % 2  # ids that alternate
+    st = Z.ShardStep(numels, nd, nd - 1, cap, BF16, groups=list(groups))
+    pl = oracle.plan(numels, nd, nd - 1, cap, groups)
+    assert (st.summary.n_buckets, st.summary.shard_numel) == (pl.n_buckets, pl.shard_len)
+    for i in range(n):
+        info = Z.zero_plan_param_info(st.plan, i)
+        assert [info.numel, info.pad, info.padded_numel, info.shard_size, info.shard_start, info.shard_end,
+                info.shard_offset, info.bucket, info.bucket_col] == list(pl.params[i]), i
+    for b in range(pl.n_buckets):
+        bk = Z.zero_plan_bucket_info(st.plan, b)
+        assert [bk.first_param, bk.n_params, bk.row_elems, bk.row_stride, bk.shard_base] == list(pl.buckets[b])
+        members = groups[bk.first_param:bk.first_param + bk.n_params]
+        assert np.all(members == members[0])  # a bucket never spans two runs of ids
+
+
+@pytest.mark.parametrize("nd,rank,dtype", [(8, 3, BF16), (64, 17, FP16)])
+def test_zero3_step_matches_oracle(nd, rank, dtype):
+    n_layers, d, vocab = 3, 48, 500
+    numels, groups = layered_model(n_layers, d, vocab)
+    say(f"zero3 nd={nd} rank={rank} layers={n_layers + 2}")
+    st = Z.ShardStep(numels, nd, rank, 0, dtype, groups=groups)
+    pl = oracle.plan(numels, nd, rank, 0, np.array(groups, np.int32))
+    assert pl.n_buckets == n_layers + 2  # one bucket per layer
+    rng = np.random.default_rng(nd + rank)
+    S = pl.shard_len
+    # every rank holds its row of every layer: the all-gather blocks start as the packed model
+    lp = [random_bits(rng, x) & np.uint16(0xBBFF) for x in numels]
+    arena = np.zeros(nd * S, np.uint16)
+    for b in range(pl.n_buckets):
+        oracle_block(pl, arena, b)[:] = oracle.pack_bucket(pl, b, lp)
+    st.arena.copy_(to_dev16(arena))
+    p32 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    st.p32.copy_(torch.from_numpy(p32))
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    steps = np.zeros(len(numels), np.int32)
+    live = np.ones(len(numels), np.uint8)
+    live[[3, 4]] = 0  # two parameters of layer 1 without a gradient (the layer-drop mapping)
+    st.live.copy_(torch.from_numpy(live))
+    z3 = Z.Zero3Schedule(st)
+
+    def check_gather(lid, params):
+        outs = [np.zeros(x, np.uint16) for x in numels]
+        oracle.unpack_bucket(pl, lid, oracle_block(pl, arena, lid).copy(), outs)
+        for i, view in zip(z3.layers[lid], params):
+            assert np.array_equal(to_np16(view), outs[i]), (lid, i)
+            assert np.array_equal(outs[i], lp[i])  # the gather restores the full parameter
+
+    grads = [random_bits(rng, x) & np.uint16(0xBBFF) for x in numels]
+    gdev = Z.ptr_table([to_dev16(g) if l else None for g, l in zip(grads, live)])
+    rows = [random_bits(rng, nd * int(pl.buckets[b, oracle.B_STRIDE])).reshape(nd, -1) & np.uint16(0xBBFF)
+            for b in range(pl.n_buckets)]
+    for b in range(pl.n_buckets):  # this rank's own row comes from its own gradients
+        rows[b][rank] = oracle.pack_bucket(pl, b, [g if l else None for g, l in zip(grads, live)])[rank]
+    rdev = [to_dev16(r.reshape(-1)) for r in rows]
+    st.flag.zero_()
+    st.g32.fill_(-3.0)
+    z3.forward(check_gather)
+    z3.backward(lambda lid: gdev, lambda lid: (rdev[lid], int(pl.buckets[lid, oracle.B_STRIDE])), check_gather)
+    assert z3.order == [0, 1, 2, 3, 4, 3, 2, 1, 0]  # the last layer is not gathered twice
+    g32 = np.full(S, -3.0, np.float32)
+    for b in range(pl.n_buckets):
+        oracle.reduce_bucket(pl, b, rows[b], dtype, live, g32)
+    torch.cuda.synchronize()
+    assert_same_f32(to_np32(st.g32), g32, "g32")
+    assert int(st.flag.item()) == oracle.overflow(pl, g32, live) == 0
+    hp = oracle.AdamHP(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, grad_scale=1.0 / nd)
+    st.adam(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.grad_scale)
+    oracle.adam(pl, g32, p32, m, v, live, steps, hp, 0, arena, dtype)
+    assert np.array_equal(to_np32(st.steps), steps)
+    assert_close_f32(to_np32(st.p32), p32, "p32")
+    assert_close_f32(to_np32(st.m), m, "m")
+    assert_close_f32(to_np32(st.v), v, "v")
+    ever = np.zeros(S, dtype=bool)
+    for i in np.flatnonzero(live):
+        ever[pl.params[i, oracle.P_OFFSET]:pl.params[i, oracle.P_OFFSET] + pl.params[i, oracle.P_SHARD]] = True
+    check_arena(pl, to_np16(st.arena), arena, to_np32(st.p32), p32, ever, dtype, "arena")
+    # model states at stage 3 against the accounting of the ZeRO summary (16 Psi / Nd)
+    psi = float(pl.params[:, oracle.P_PADDED].sum())
+    assert Z.zero_plan_model_state_bytes(st.plan, 3) == pytest.approx(16 * psi / nd)
+    # at most one layer's full parameters at a time: the scratch holds the largest layer
+    biggest = max(sum(numels[i] for i in z3.layers[b]) for b in range(pl.n_buckets))
+    assert biggest <= z3.scratch.numel() < biggest + 8 * 8

@@ -21,7 +21,7 @@ ZERO_BF16, ZERO_FP16 = 1, 2
 STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_ENOMEM", -3: "ZERO_EHIP", -4: "ZERO_ERANGE"}
 
 # Every symbol the header declares (checked against the header by the ABI test).
-EXPORTS = ("zero_plan_create", "zero_plan_destroy", "zero_plan_get_summary", "zero_plan_param_info",
+EXPORTS = ("zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy", "zero_plan_get_summary", "zero_plan_param_info",
            "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes", "zero_pack_bucket",
            "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack", "zero_shard_init",
            "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket", "zero_loss_scaler_init",
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
     i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
     sigs = {
         "zero_plan_create": (i32, [vp, i64, i32, i32, i64, i32, ctypes.POINTER(vp)]),
+        "zero_plan_create_grouped": (i32, [vp, vp, i64, i32, i32, i64, i32, ctypes.POINTER(vp)]),
         "zero_plan_destroy": (None, [vp]),
         "zero_plan_get_summary": (i32, [vp, ctypes.POINTER(zero_plan_summary)]),
         "zero_plan_param_info": (i32, [vp, i64, ctypes.POINTER(zero_param_info)]),
@@ -160,6 +161,17 @@ def zero_plan_create(numels: Sequence[int], nd: int, rank: int, bucket_bytes: in
     arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
     out = ctypes.c_void_p()
     _check(lib().zero_plan_create(arr, len(numels), nd, rank, bucket_bytes, dtype, ctypes.byref(out)))
+    return Plan(out.value)
+
+
+def zero_plan_create_grouped(numels: Sequence[int], groups: Optional[Sequence[int]], nd: int, rank: int,
+                             bucket_bytes: int, dtype: int) -> Plan:
+    arr = (ctypes.c_int64 * max(len(numels), 1))(*[int(x) for x in numels])
+    if groups is not None and len(groups) != len(numels):
+        raise ValueError("one group id per parameter")
+    garr = None if groups is None else (ctypes.c_int32 * max(len(groups), 1))(*[int(x) for x in groups])
+    out = ctypes.c_void_p()
+    _check(lib().zero_plan_create_grouped(arr, garr, len(numels), nd, rank, bucket_bytes, dtype, ctypes.byref(out)))
     return Plan(out.value)
 
 

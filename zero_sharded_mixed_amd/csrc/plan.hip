@@ -134,19 +134,21 @@ __global__ __launch_bounds__(kScanThreads) void plan_scan_kernel(PlanScratch T, 
 }
 
 // One thread: walk the list into buckets.  A bucket starting at i0 takes the longest run
-// i0..i1 whose padded total fits the capacity (found by binary search over the inclusive
-// scan), and at least i0 itself.  capacity < 0 means unbounded.
-__global__ void plan_buckets_kernel(PlanScratch T, int64_t n, int64_t capacity) {
+// i0..i1 that stays inside i0's group (i1 <= gend[i0], the last index of that group) and whose
+// padded total fits the capacity (found by binary search over the inclusive scan), and at
+// least i0 itself.  capacity < 0 means unbounded.
+__global__ void plan_buckets_kernel(PlanScratch T, const int64_t* __restrict__ gend, int64_t n, int64_t capacity) {
     if (blockIdx.x != 0 || threadIdx.x != 0) return;
     int64_t i0 = 0, nb = 0, base = 0;
     const int64_t total_s = T.totals[2];
     while (i0 < n) {
         int64_t i1;
+        const int64_t last = gend[i0];
         if (capacity < 0) {
-            i1 = n - 1;
+            i1 = last;
         } else {
             const int64_t prev = i0 > 0 ? T.pp[i0 - 1] : 0;
-            int64_t lo = i0, hi = n;  // first i in [i0, n) with pp[i] - prev > capacity
+            int64_t lo = i0, hi = last + 1;  // first i in [i0, last] with pp[i] - prev > capacity
             while (lo < hi) {
                 const int64_t mid = (lo + hi) >> 1;
                 if (T.pp[mid] - prev > capacity) hi = mid; else lo = mid + 1;
@@ -226,8 +228,9 @@ extern "C" void zero_plan_destroy(zero_plan* plan) {
     delete plan;
 }
 
-extern "C" zero_status zero_plan_create(const int64_t* numels, int64_t n_params, int32_t nd, int32_t rank,
-                                        int64_t bucket_bytes, int32_t dtype, zero_plan** out) {
+extern "C" zero_status zero_plan_create_grouped(const int64_t* numels, const int32_t* groups, int64_t n_params,
+                                                int32_t nd, int32_t rank, int64_t bucket_bytes, int32_t dtype,
+                                                zero_plan** out) {
     if (!out) return fail(ZERO_EINVAL, "zero_plan_create: out is NULL");
     *out = nullptr;
     if (!numels) return fail(ZERO_EINVAL, "zero_plan_create: numels is NULL");
@@ -273,7 +276,8 @@ extern "C" zero_status zero_plan_create(const int64_t* numels, int64_t n_params,
                      o_col = take(8 * n8), o_dense = take(8 * n8), o_pp = take(8 * n8), o_uc = take(8 * n8),
                      o_ucb = take(8 * n8), o_ucend = take(8 * n8), o_invs = take(8 * n8), o_bucket = take(4 * n8),
                      o_bfirst = take(4 * n8), o_bcount = take(4 * n8), o_brow = take(8 * n8), o_bstride = take(8 * n8),
-                     o_bbase = take(8 * n8), o_totals = take(8 * 8), o_in = take(8 * n8), o_scal = take(8 * n8),
+                     o_bbase = take(8 * n8), o_totals = take(8 * 8), o_in = take(8 * n8), o_gend = take(8 * n8),
+                     o_scal = take(8 * n8),
                      o_const = take(4 * 8);
         // Tile maps are sized once the totals are known; reserve a generous upper bound now
         // so everything lives in one allocation: shard columns <= padded total / nd + 8 * n.
@@ -312,6 +316,7 @@ extern "C" zero_status zero_plan_create(const int64_t* numels, int64_t n_params,
         T.b_base = (int64_t*)(m + o_bbase);
         T.totals = (int64_t*)(m + o_totals);
         d_numels_in = (int64_t*)(m + o_in);
+        int64_t* d_gend = (int64_t*)(m + o_gend);
         P->d_adam_scal = (float*)(m + o_scal);
         P->d_adam_const = (float*)(m + o_const);
         int32_t* d_tile = (int32_t*)(m + o_tile);
@@ -319,12 +324,17 @@ extern "C" zero_status zero_plan_create(const int64_t* numels, int64_t n_params,
 
         hipStream_t s = nullptr;
         ZS_HIP(hipMemcpy(d_numels_in, numels, 8 * size_t(n), hipMemcpyHostToDevice), "upload numels");
+        // gend[i]: the last index of the run of equal group ids holding i (n - 1 without groups)
+        tmp.assign(static_cast<size_t>(n), n - 1);
+        if (groups)
+            for (int64_t i = n - 2; i >= 0; --i) tmp[i] = groups[i] == groups[i + 1] ? tmp[i + 1] : i;
+        ZS_HIP(hipMemcpy(d_gend, tmp.data(), 8 * size_t(n), hipMemcpyHostToDevice), "upload groups");
         const int g = grid_for((n + 255) / 256, 1024);
         plan_fields_kernel<<<g, 256, 0, s>>>(T, d_numels_in, n, nd, rank);
         if ((st = check_launch("plan_fields_kernel")) != ZERO_OK) goto done;
         plan_scan_kernel<<<1, kScanThreads, 0, s>>>(T, n);
         if ((st = check_launch("plan_scan_kernel")) != ZERO_OK) goto done;
-        plan_buckets_kernel<<<1, 64, 0, s>>>(T, n, bucket_bytes > 0 ? bucket_bytes / 2 : -1);
+        plan_buckets_kernel<<<1, 64, 0, s>>>(T, d_gend, n, bucket_bytes > 0 ? bucket_bytes / 2 : -1);
         if ((st = check_launch("plan_buckets_kernel")) != ZERO_OK) goto done;
         plan_place_kernel<<<g, 256, 0, s>>>(T, n);
         if ((st = check_launch("plan_place_kernel")) != ZERO_OK) goto done;
@@ -426,6 +436,11 @@ done:
     }
     *out = P;
     return ZERO_OK;
+}
+
+extern "C" zero_status zero_plan_create(const int64_t* numels, int64_t n_params, int32_t nd, int32_t rank,
+                                        int64_t bucket_bytes, int32_t dtype, zero_plan** out) {
+    return zero_plan_create_grouped(numels, nullptr, n_params, nd, rank, bucket_bytes, dtype, out);
 }
 
 extern "C" zero_status zero_plan_get_summary(const zero_plan* plan, zero_plan_summary* out) {

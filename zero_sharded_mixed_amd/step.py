@@ -16,9 +16,13 @@ from . import _binding as B
 
 
 class ShardStep:
-    def __init__(self, numels: Sequence[int], nd: int, rank: int, bucket_bytes: int, dtype: int, device="cuda"):
+    def __init__(self, numels: Sequence[int], nd: int, rank: int, bucket_bytes: int, dtype: int, device="cuda",
+                 groups: Optional[Sequence[int]] = None):
+        """groups: one id per parameter (a bucket never spans a change of id), e.g. the layer
+        index, giving ZeRO-3's one bucket per layer with bucket_bytes = 0."""
         self.device = torch.device(device)
-        self.plan = B.zero_plan_create(numels, nd, rank, bucket_bytes, dtype)
+        self.plan = (B.zero_plan_create(numels, nd, rank, bucket_bytes, dtype) if groups is None else
+                     B.zero_plan_create_grouped(numels, groups, nd, rank, bucket_bytes, dtype))
         self.summary = B.zero_plan_get_summary(self.plan)
         s = self.summary
         self.nd, self.rank, self.dtype = nd, rank, dtype
@@ -110,3 +114,71 @@ class ShardStep:
 
     def close(self) -> None:
         self.plan.close()
+
+
+class Zero3Schedule:
+    """ZeRO-3's per-layer parameter traffic over a ShardStep whose plan has one bucket per
+    layer (groups = layer index, bucket_bytes = 0), following the llm-engineer "ZeRO-3" card:
+    before a layer runs, its parameters are all-gathered into a scratch buffer, used and freed;
+    the forward pass gathers layers 0, 1, ..., L-1, the backward pass keeps the last layer and
+    gathers L-2, ..., 0 again (the 0 -> 1 -> 2 -> 1 -> 0 order for three layers); each layer's
+    gradients are reduce-scattered (pack + reduce) as soon as its backward has run.
+
+    The gather of layer l is zero_unpack of bucket l from the all-gather block (the Nd ranks'
+    rows of that layer); its destination is one scratch buffer sized for the largest layer, so
+    at most one layer's full parameters exist at a time."""
+
+    def __init__(self, st: ShardStep):
+        self.st = st
+        nb = len(st.buckets)
+        infos = [B.zero_plan_param_info(st.plan, i) for i in range(st.n)]
+        self.layers = [list(range(int(bk.first_param), int(bk.first_param + bk.n_params))) for bk in st.buckets]
+        self.numel = [[int(infos[i].numel) for i in params] for params in self.layers]
+        biggest = max((sum(x) for x in self.numel), default=0)
+        # each parameter 16-byte aligned inside the scratch (the unpack's wide path)
+        per = [sum((x + 7) // 8 * 8 for x in xs) for xs in self.numel]
+        self.scratch = torch.zeros(max(per + [biggest, 8]), dtype=torch.int16, device=st.device)
+        self.views, self.tables = [], []
+        for lid in range(nb):
+            views, pos = [], 0
+            for x in self.numel[lid]:
+                views.append(self.scratch[pos:pos + x])
+                pos += (x + 7) // 8 * 8
+            full = [None] * st.n
+            for i, v in zip(self.layers[lid], views):
+                full[i] = v
+            self.views.append(views)
+            self.tables.append(B.ptr_table(full, device=st.device))
+        self.order: list = []  # layers in the order they were gathered
+
+    def gather(self, lid: int, src: Optional[torch.Tensor] = None, stream=None) -> list:
+        """All-gather layer lid's parameters (the unpack of its bucket) into the scratch buffer;
+        returns one view per parameter, valid until the next gather."""
+        st = self.st
+        src = st.arena if src is None else src
+        B.zero_unpack(st.plan, lid, st.block(src, lid), self.tables[lid], stream)
+        self.order.append(lid)
+        return self.views[lid]
+
+    def forward(self, use: Optional[Callable[[int, list], None]] = None, stream=None) -> None:
+        for lid in range(len(self.layers)):
+            params = self.gather(lid, stream=stream)
+            if use is not None:
+                use(lid, params)
+
+    def backward(self, grads_of: Callable[[int], torch.Tensor], rows_of: Callable[[int], tuple],
+                 use: Optional[Callable[[int, list], None]] = None, check: bool = False, stream=None) -> None:
+        """grads_of(l): pointer table of this rank's gradients (entries of layer l used);
+        rows_of(l): (rows of bucket l from the Nd ranks, row stride) for the reduce-scatter."""
+        st = self.st
+        last = len(self.layers) - 1
+        for lid in range(last, -1, -1):
+            params = self.views[lid] if lid == last else self.gather(lid, stream=stream)
+            if use is not None:
+                use(lid, params)
+            if check:
+                B.zero_pack_bucket_check(st.plan, lid, grads_of(lid), st.block(st.packed, lid), st.flag, stream)
+            else:
+                B.zero_pack_bucket(st.plan, lid, grads_of(lid), st.block(st.packed, lid), stream)
+            rows, stride = rows_of(lid)
+            B.zero_reduce_shard(st.plan, lid, rows, stride, st.live, st.g32, st.flag, stream)
