@@ -253,6 +253,86 @@ def run_gpu(w, ctx, path, steps, warmup):
     return wall / steps * 1e3, per_phase, {p: launches[p] for p in phases}, flag
 
 
+def run_zero3(w, ctx, steps, warmup, device):
+    """ZeRO-3's step on the same list with one bucket per layer (workloads.layer_groups): the
+    forward pass gathers every layer's parameters (unpack into a scratch buffer), the backward
+    pass gathers all but the last layer again and reduce-scatters each layer's gradients (pack
+    + reduce) right after it, then Adam writes this rank's 16-bit shard.  Full emulation: every
+    virtual rank's gradients are packed for the per-layer buckets beforehand; this rank's are
+    re-packed inside each timed step, into the rows the reduce reads."""
+    import workloads as W
+
+    st2, own_ptrs, _, _, lp, lp_ptrs, live = ctx
+    t0 = time.time()
+    z = Z.ShardStep(w.numels, w.nd, w.rank, 0, w.dtype, device=device, groups=W.layer_groups(w))
+    z.live.copy_(st2.live)
+    z.init_master(lp_ptrs, w.dtype)  # p32 = row r of the 16-bit model (converted exactly)
+    z.pack(lp_ptrs, out=z.arena)     # every rank holds its row of every layer
+    an = int(z.summary.arena_numel)
+    packed_all = torch.empty((w.nd, an), dtype=torch.int16, device=device)
+    for k in range(w.nd):
+        if k == w.rank:
+            z.pack(own_ptrs, out=packed_all[k])
+            continue
+        g = [t if l else None for t, l in zip(W.grads(w, 0, k, device), live)]
+        z.pack(Z.ptr_table(g), out=packed_all[k])
+        del g
+    flat = packed_all.view(-1)
+
+    def rows_of(b):
+        bk = z.buckets[b]
+        return flat[bk.block_offset + w.rank * bk.row_stride:], an
+
+    z3 = Z.Zero3Schedule(z)
+    torch.cuda.synchronize()
+    log(f"[bench] zero3: {len(z.buckets)} layer buckets, scratch {z3.scratch.numel()} elements "
+        f"({time.time() - t0:.1f}s)")
+    b1, b2 = w.betas
+    phases = ("forward", "backward", "adam")
+
+    def one_step(ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+
+        mark(0)
+        z.flag.zero_()
+        z3.order.clear()
+        z3.forward()
+        mark(1)
+        z3.backward(lambda lid: own_ptrs, rows_of, out=packed_all[w.rank])
+        mark(2)
+        z.adam(w.lr, b1, b2, w.eps, w.grad_scale)
+        mark(3)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
+    t1 = time.perf_counter()
+    for i in range(steps):
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t1) / steps * 1e3
+    per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j, p in enumerate(phases)}
+    shard_sizes = [Z.zero_plan_param_info(z.plan, i).shard_size for i in range(z.n)]
+    ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
+    numel_all = int(sum(int(x) for x in w.numels))
+    last = z3.layers[-1]
+    numel_last = int(sum(int(w.numels[i]) for i in last))
+    nbytes = {"forward": 4 * numel_all, "backward": 4 * (numel_all - numel_last) + ab["pack"] + ab["reduce"],
+              "adam": ab["adam"]}
+    total = sum(nbytes.values())
+    out = {"ms_per_step": round(wall, 4), "GBs": round(total / (wall * 1e-3) / 1e9, 1), "step_bytes": total,
+           "elem_per_s": round(ab["shard_live"] / (wall * 1e-3), 1), "layers": len(z.buckets),
+           "gathers_per_step": len(z3.order), "overflow_flag": int(z.flag.item()),
+           "phases": {p: {"ms": round(per[p], 4), "bytes": nbytes[p],
+                          "GBs": round(nbytes[p] / (per[p] * 1e-3) / 1e9, 1)} for p in phases}}
+    del packed_all, z3, z
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_reference(device, nbytes=2 << 30, reps=10):
     """GB/s (read + write) of torch's device-to-device copy of a 2 GiB buffer: what a plain
     streaming kernel reaches on this device, for context next to the 8 TB/s peak."""
@@ -432,6 +512,7 @@ def main():
     ap.add_argument("--cpu-sample-elems", type=int, default=1_600_000_000,
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-zero3", action="store_true", help="skip the ZeRO-3 (one bucket per layer) leg")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="reduce rocprofv3 CSVs under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/) to a text summary "
                          "on stdout and profiles/traffic.json, then exit")
@@ -470,6 +551,9 @@ def main():
              "GBs": round(fz["bytes"] / (fz["ms"] * 1e-3) / 1e9, 1), "step_bytes": fz["bytes"],
              "elem_per_s": round(ab["shard_live"] / (fz["ms"] * 1e-3), 1), "overflow_flag": fz["flag"],
              "kernels": fz["kernels"]}
+    zero3 = None
+    if w.emulation == "full" and not args.no_zero3:
+        zero3 = run_zero3(w, ctx, args.steps, args.warmup, device)
     fk = fz["kernels"]["reduce_adam"]
     fused["roofline"] = {"bound": "hbm", "kernel": "reduce_adam", "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "achieved": fk["GBs"], "frac": fk["frac"],
@@ -505,6 +589,7 @@ def main():
         "overflow_flag": flag,
         "kernels": kernels,
         "fused": fused,
+        "zero3": zero3,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["bytes"] / launches[dom] /
                                                                       (d["ms"] / launches[dom] * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],

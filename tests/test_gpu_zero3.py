@@ -118,3 +118,100 @@ def test_zero3_step_matches_oracle(nd, rank, dtype):
     # at most one layer's full parameters at a time: the scratch holds the largest layer
     biggest = max(sum(numels[i] for i in z3.layers[b]) for b in range(pl.n_buckets))
     assert biggest <= z3.scratch.numel() < biggest + 8 * 8
+
+
+@pytest.mark.timeout(900)
+def test_zero3_fullsize_gpt2_matches_zero2_and_oracle():
+    """The GPT-2 1.5B-shaped list at Nd = 8 with one bucket per layer, as bench.py's ZeRO-3 leg
+    runs it: every forward gather restores its layer's parameters exactly; after the step,
+    p32 / m / v and this rank's 16-bit shard equal the ZeRO-2 step's (same gradients, 500M-element
+    buckets) parameter by parameter, bit for bit; sampled columns against the oracle."""
+    import workloads as W
+    from gpu_harness import bits16, column_owner, gather_params, sample_columns
+
+    w = W.workload(2)
+    nd, r = w.nd, w.rank
+    groups = W.layer_groups(w)
+    A = Z.ShardStep(w.numels, nd, r, w.bucket_bytes, w.dtype)      # ZeRO-2 buckets
+    G = Z.ShardStep(w.numels, nd, r, 0, w.dtype, groups=groups)   # ZeRO-3: one bucket per layer
+    assert len(G.buckets) == max(groups) + 1
+    pl = oracle.plan(w.numels, nd, r, 0, np.array(groups, np.int32))
+    rng = np.random.default_rng(33)
+    cols = sample_columns(pl, rng, 4000)
+    ci, cj = column_owner(pl, cols)
+    ce = r * pl.params[ci, oracle.P_SHARD] + cj
+    masters = W.masters(w, DEV)
+    for X in (A, G):
+        X.init_master(Z.ptr_table(masters), 0)
+    p0 = gather_params(masters, ci, ce, 0.0).numpy().astype(np.float32)  # row r of the padded master
+    p0[ce >= pl.params[ci, oracle.P_NUMEL]] = 0.0
+    lp = [m.to(torch.bfloat16) for m in masters]
+    del masters
+    lp_ptrs = Z.ptr_table(lp)
+    for X in (A, G):
+        X.pack(lp_ptrs, out=X.arena)
+    live = W.live_mask(w, 0)
+    pa = torch.empty((nd, int(A.summary.arena_numel)), dtype=torch.int16, device=DEV)
+    pg = torch.empty((nd, int(G.summary.arena_numel)), dtype=torch.int16, device=DEV)
+    own = None
+    for k in range(nd):
+        g = [t if l else None for t, l in zip(W.grads(w, 0, k, DEV), live)]
+        A.pack(Z.ptr_table(g), out=pa[k])
+        G.pack(Z.ptr_table(g), out=pg[k])
+        if k == r:
+            own = g
+    own_ptrs = Z.ptr_table(own)
+    say("[zero3 fullsize] inputs resident")
+    # ZeRO-2
+    A.reduce(lambda b: (pa.view(-1)[A.buckets[b].block_offset + r * A.buckets[b].row_stride:], pa.shape[1]))
+    hp = (w.lr, w.betas[0], w.betas[1], w.eps, w.grad_scale)
+    A.adam(*hp)
+    # ZeRO-3
+    z3 = Z.Zero3Schedule(G)
+
+    def restored(lid, params):
+        for i, view in zip(z3.layers[lid], params):
+            assert torch.equal(view, lp[i].view(torch.int16)), (lid, i)
+
+    z3.forward(restored)
+    z3.backward(lambda lid: own_ptrs,
+                lambda b: (pg.view(-1)[G.buckets[b].block_offset + r * G.buckets[b].row_stride:], pg.shape[1]),
+                restored, out=pg[r])
+    G.adam(*hp)
+    torch.cuda.synchronize()
+    assert int(A.flag.item()) == int(G.flag.item()) == 0
+    assert z3.order == list(range(len(G.buckets))) + list(range(len(G.buckets) - 2, -1, -1))
+    assert torch.equal(A.steps, G.steps)
+    for i in range(A.n):
+        ia, ig = Z.zero_plan_param_info(A.plan, i), Z.zero_plan_param_info(G.plan, i)
+        s = int(ia.shard_size)
+        for ta, tg in ((A.p32, G.p32), (A.m, G.m), (A.v, G.v)):
+            assert torch.equal(ta[ia.shard_offset:ia.shard_offset + s].view(torch.int32),
+                               tg[ig.shard_offset:ig.shard_offset + s].view(torch.int32)), i
+        ba, bg = A.buckets[ia.bucket], G.buckets[ig.bucket]
+        ra = ba.block_offset + r * ba.row_stride + ia.bucket_col
+        rg = bg.block_offset + r * bg.row_stride + ig.bucket_col
+        assert torch.equal(A.arena[ra:ra + s], G.arena[rg:rg + s]), i
+    # the oracle on sampled columns of the per-layer plan: virtual rank k's value at column c of
+    # bucket b is element nd * O_b + r * L_b + c of its packed buffer pg[k]
+    cb = pl.params[ci, oracle.P_BUCKET]
+    cc = pl.params[ci, oracle.P_COL] + cj
+    rows = np.zeros((nd, cols.size), np.uint16)
+    flat = pg.view(-1)
+    for k in range(nd):
+        if k == r:
+            real = ce < pl.params[ci, oracle.P_NUMEL]
+            rows[k] = np.where(real, bits16(gather_params(own, ci, ce, 0)), 0)  # from the gradients themselves
+        else:
+            idx = torch.from_numpy(k * pg.shape[1] + nd * pl.buckets[cb, oracle.B_BASE] +
+                                   r * pl.buckets[cb, oracle.B_STRIDE] + cc)
+            rows[k] = bits16(flat[idx.to(DEV)].cpu())
+    ohp = oracle.AdamHP(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps, grad_scale=w.grad_scale)
+    want = [oracle.adam_element(oracle.reduce_column(rows[:, t], w.dtype), p0[t], 0.0, 0.0, 1, ohp)
+            for t in range(cols.size)]
+    cols_dev = torch.from_numpy(cols).to(DEV)
+    assert_close_f32(to_np32(G.p32[cols_dev]), np.array([x[0] for x in want], np.float32), "p32")
+    assert_close_f32(to_np32(G.m[cols_dev]), np.array([x[1] for x in want], np.float32), "m")
+    assert_close_f32(to_np32(G.v[cols_dev]), np.array([x[2] for x in want], np.float32), "v")
+    del pa, pg, own, lp, A, G, z3
+    torch.cuda.empty_cache()

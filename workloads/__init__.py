@@ -157,6 +157,29 @@ def workload(config: int) -> Workload:
     raise ValueError(f"no workload {config}")
 
 
+def layer_groups(w: Workload) -> list:
+    """One id per parameter naming its ZeRO-3 unit (the llm-engineer "ZeRO-3" card gathers and
+    frees parameters one layer at a time): the parameters before the first transformer block
+    (embeddings), each block ("h.<l>." / "layers.<l>."), and the parameters after the last block
+    (final norm, untied head).  Lists without blocks: one unit per module (the name up to its
+    last dot)."""
+    names = [n for n, _ in w.params]
+    blocks = any(n.startswith(("h.", "layers.")) for n in names)
+    keys, seen = [], False
+    for n in names:
+        if n.startswith(("h.", "layers.")):
+            keys.append(".".join(n.split(".")[:2]))
+            seen = True
+        elif blocks:
+            keys.append("after" if seen else "before")
+        else:
+            keys.append(n.rsplit(".", 1)[0])
+    ids = []
+    for j, k in enumerate(keys):  # runs of equal keys, numbered in list order
+        ids.append(0 if j == 0 else ids[-1] + (k != keys[j - 1]))
+    return ids
+
+
 # ----------------------------------------------------------------- random values ------
 
 def _gen(seed: int, device) -> torch.Generator:

@@ -167,18 +167,21 @@ class Zero3Schedule:
                 use(lid, params)
 
     def backward(self, grads_of: Callable[[int], torch.Tensor], rows_of: Callable[[int], tuple],
-                 use: Optional[Callable[[int, list], None]] = None, check: bool = False, stream=None) -> None:
+                 use: Optional[Callable[[int, list], None]] = None, check: bool = False,
+                 out: Optional[torch.Tensor] = None, stream=None) -> None:
         """grads_of(l): pointer table of this rank's gradients (entries of layer l used);
-        rows_of(l): (rows of bucket l from the Nd ranks, row stride) for the reduce-scatter."""
+        rows_of(l): (rows of bucket l from the Nd ranks, row stride) for the reduce-scatter;
+        out: where the packed gradient blocks go (arena layout; default st.packed)."""
         st = self.st
+        out = st.packed if out is None else out
         last = len(self.layers) - 1
         for lid in range(last, -1, -1):
             params = self.views[lid] if lid == last else self.gather(lid, stream=stream)
             if use is not None:
                 use(lid, params)
             if check:
-                B.zero_pack_bucket_check(st.plan, lid, grads_of(lid), st.block(st.packed, lid), st.flag, stream)
+                B.zero_pack_bucket_check(st.plan, lid, grads_of(lid), st.block(out, lid), st.flag, stream)
             else:
-                B.zero_pack_bucket(st.plan, lid, grads_of(lid), st.block(st.packed, lid), stream)
+                B.zero_pack_bucket(st.plan, lid, grads_of(lid), st.block(out, lid), stream)
             rows, stride = rows_of(lid)
             B.zero_reduce_shard(st.plan, lid, rows, stride, st.live, st.g32, st.flag, stream)
