@@ -522,8 +522,8 @@ def main():
         print(summarize_profiles(args.summarize_profiles, WORKLOAD_IDS[args.config], args.profile_command), end="")
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU reduce-scatter/all-gather path is not built)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU reduce-scatter/all-gather path is not implemented)", file=sys.stderr)
         sys.exit(2)
     import workloads as W
 

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "zero_shard.h")
 
 @pytest.fixture(scope="module")
 def L():
-    if not os.path.exists(B.LIB_PATH):  # CPU-only container: build it (never on the GPU machine)
+    if not os.path.exists(B.LIB_PATH):  # not built yet: build it (hipcc cross-compiles without a GPU)
         from zero_sharded_mixed_amd import build
         build.build()
     return Z.lib()
