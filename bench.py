@@ -32,8 +32,10 @@ import zero_sharded_mixed_amd as Z  # noqa: E402  (fails at first call if the HI
 HBM_PEAK_GBS = 8000.0
 METRIC = "shard step GB/s & elem/s (pack+reduce+Adam) vs HBM peak, 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-WORKLOAD_IDS = {2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63", 5: "ragged-10k-nd1024-r517"}
+WORKLOAD_IDS = {1: "mlp-nd8-r3", 2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63", 5: "ragged-10k-nd1024-r517"}
 WORKLOAD_TEXT = {
+    1: "MlpModel (Linear(128,256), Linear(256,256) never called, Linear(256,512)); Nd=8, rank 3, one bucket; "
+       "bf16 grads N(0,1e-2); fp32 master / m / v (about 1 MB: launch-bound)",
     2: "GPT-2 1.5B-shaped parameter list (48 layers, d=1600, vocab 50257, 1024 positions); Nd=8 virtual ranks, "
        "rank 0, 500M-element buckets; bf16 grads N(0,1e-3) and params, fp32 master N(0,0.02) / m / v; Adam lr 1e-3, "
        "betas (0.9, 0.999), eps 1e-8",
@@ -506,9 +508,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5),
-                    help="workload: 2 = GPT-2 1.5B-shaped list (the default and the reported line); 3 Llama-7B, "
-                         "4 7.5B paper-style at Nd=64, 5 ragged at Nd=1024 (informational)")
+    ap.add_argument("--config", type=int, default=2, choices=(1, 2, 3, 4, 5),
+                    help="workload: 2 = GPT-2 1.5B-shaped list (the default and the reported line); 1 MlpModel "
+                         "(launch-bound), 3 Llama-7B, 4 7.5B paper-style at Nd=64, 5 ragged at Nd=1024 (informational)")
     ap.add_argument("--cpu-sample-elems", type=int, default=1_600_000_000,
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
