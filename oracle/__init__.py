@@ -34,13 +34,17 @@ B_FIRST, B_COUNT, B_ROW, B_STRIDE, B_BASE = range(5)
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fexcess-precision=standard",
              "-fPIC", "-shared", "-Wall", "-Werror"]
+# ORACLE_SANITIZE=1: build with AddressSanitizer and UBSan (host code; run the tests with
+# LD_PRELOAD of gcc's libasan.so and libubsan.so and ASAN_OPTIONS=detect_leaks=0)
+SANITIZE_FLAGS = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
 
 
 def build_library(force: bool = True) -> str:
     """Compile zero_oracle.c with gcc into libzero_oracle.so next to it."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        extra = SANITIZE_FLAGS if os.environ.get("ORACLE_SANITIZE") == "1" else []
+        subprocess.run(["gcc", *GCC_FLAGS, *extra, "-o", tmp, _SRC, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
