@@ -12,8 +12,8 @@ import torch
 import oracle
 import workloads as W
 import zero_sharded_mixed_amd as Z
-from gpu_harness import (DEV, assert_close_f32, bits16, check_arena, column_owner, gather_params, ragged_numels,
-                         random_bits, row_zero_mask, sample_columns, say, to_dev16, to_np16, to_np32)
+from gpu_harness import (DEV, assert_close_f32, bits16, check_arena, column_owner, gather_params, placed_views,
+                         ragged_numels, random_bits, row_zero_mask, sample_columns, say, to_dev16, to_np16, to_np32)
 
 pytestmark = pytest.mark.gpu
 BF16, FP16 = Z.ZERO_BF16, Z.ZERO_FP16
@@ -121,6 +121,40 @@ def test_checked_pack(case, dtype):
             dev[i][e] = int(np.uint16(old).view(np.int16))
             trials += 1
     assert trials == 18
+
+
+@pytest.mark.parametrize("case", [CASES[2], CASES[3]])
+def test_checked_pack_misaligned_gradients(case):
+    """Gradients at odd 2-byte offsets (realigned loads, staged and element paths): the same
+    bits as the oracle's pack and the same verdict, clean and with one injection per trial."""
+    nd, rank, cap, seed = case
+    rng = np.random.default_rng(seed + 500)
+    numels = layout_numels(rng, nd)
+    st = Z.ShardStep(numels, nd, rank, cap, BF16)
+    pl = oracle.plan(numels, nd, rank, cap)
+    grads = [finite_bits(rng, x, BF16) for x in numels]
+    buf, views = placed_views(grads, rng, misalign=True)
+    ptrs = Z.ptr_table(views)
+    for trial in range(4):
+        inj = None
+        if trial:
+            i = int(rng.choice([j for j in range(len(numels)) if numels[j] > 0]))
+            e = int(rng.integers(0, numels[i]))
+            inj = (i, e, grads[i][e])
+            grads[i][e] = 0x7FC0
+            views[i][e] = int(np.uint16(0x7FC0).view(np.int16))
+        for b in range(pl.n_buckets):
+            st.flag.zero_()
+            Z.zero_pack_bucket_check(st.plan, b, ptrs, st.block(st.packed, b), st.flag)
+            want = oracle.pack_bucket(pl, b, grads)
+            got = to_np16(st.block(st.packed, b)).reshape(want.shape)
+            assert np.array_equal(got, want), (trial, b)
+            assert int(st.flag.item()) == oracle.input_check(pl, b, grads, BF16), (trial, b)
+        if inj:
+            i, e, old = inj
+            grads[i][e] = old
+            views[i][e] = int(np.uint16(old).view(np.int16))
+    del buf
 
 
 def test_checked_pack_bound_at_nd8():
