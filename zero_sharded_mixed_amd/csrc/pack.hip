@@ -297,20 +297,15 @@ __device__ __forceinline__ void unpack_chunk(int64_t u, int64_t ucb, int64_t num
     }
 }
 
-struct UnpackMeta {
-    int64_t ucb, ucend, numel, s, col;
-    double inv_s;
-    uint16_t* out;
-};
-
 // One block iteration covers kUnpackUnroll consecutive chunk tiles (256 chunks each); a
 // thread takes one chunk of each.  Chunks of the bucket's parameters are [u0, u1).  A group
-// inside one parameter reads that parameter's fields once (scalar loads); otherwise the block
-// stages the fields of every overlapping parameter in LDS (up to kStageMax of them).
+// inside one parameter reads that parameter's fields once (scalar loads); otherwise each thread
+// finds its chunk's parameter in the chunk tile map.  The kernel uses no LDS: staging the
+// parameter fields of mixed groups in LDS, as the pack does, made every block carry a 14 KB
+// allocation and cost 4-7% on whole lists (most groups are whole), more than it saved.
 __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t u0,
                                                         int64_t u1, const uint16_t* __restrict__ gathered,
                                                         uint16_t* const* __restrict__ outs) {
-    __shared__ UnpackMeta sm[kStageMax];
     const int64_t ut0 = u0 >> kUTileShift;
     const int64_t n_ut = ((u1 + kUTileChunks - 1) >> kUTileShift) - ut0;
     const int64_t n_groups = (n_ut + kUnpackUnroll - 1) / kUnpackUnroll;
@@ -358,33 +353,7 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_bas
                 unpack_chunk(ua + t * kUTileChunks + threadIdx.x, ucb, numel, s, col, inv_s, b_stride, gathered, out);
             continue;
         }
-        // parameters overlapping the group: [iu, last]
-        const int64_t unext = ut + kUnpackUnroll <= P.n_utiles ? ut + kUnpackUnroll : P.n_utiles;
-        const int64_t inext = ld_const(P.utile_first, unext);
-        const int64_t last = inext < P.n ? inext : P.n - 1;
-        const int64_t cnt = iu < P.n ? last - iu + 1 : 0;
-        if (cnt <= kStageMax) {
-            __syncthreads();  // the previous iteration's readers are done with the stage
-            for (int64_t t = threadIdx.x; t < cnt; t += kBlock) {
-                const int64_t pi = iu + t;
-                sm[t] = UnpackMeta{P.ucb[pi], P.ucend[pi], P.numel[pi], P.s[pi], P.off[pi] - b_base, P.inv_s[pi],
-                                   outs[pi]};
-            }
-            __syncthreads();
-#pragma unroll
-            for (int t = 0; t < kUnpackUnroll; ++t) {
-                const int64_t u = ua + t * kUTileChunks + threadIdx.x;
-                if (u < u0 || u >= u1) continue;
-                int lo = 0, hi = int(cnt);  // first staged parameter with ucend > u
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (sm[mid].ucend > u) hi = mid; else lo = mid + 1;
-                }
-                const UnpackMeta& m = sm[lo];
-                if (m.out) unpack_chunk(u, m.ucb, m.numel, m.s, m.col, m.inv_s, b_stride, gathered, m.out);
-            }
-            continue;
-        }
+        // a group of several parameters: each thread finds its chunk's parameter
 #pragma unroll
         for (int t = 0; t < kUnpackUnroll; ++t) {
             const int64_t u = ua + t * kUTileChunks + threadIdx.x;
