@@ -32,7 +32,8 @@ import zero_sharded_mixed_amd as Z  # noqa: E402  (fails at first call if the HI
 HBM_PEAK_GBS = 8000.0
 METRIC = "shard step GB/s & elem/s (pack+reduce+Adam) vs HBM peak, 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-WORKLOAD_IDS = {1: "mlp-nd8-r3", 2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63", 5: "ragged-10k-nd1024-r517"}
+WORKLOAD_IDS = {1: "mlp-nd8-r3", 2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63",
+                5: "ragged-10k-nd1024-r517"}
 WORKLOAD_TEXT = {
     1: "MlpModel (Linear(128,256), Linear(256,256) never called, Linear(256,512)); Nd=8, rank 3, one bucket; "
        "bf16 grads N(0,1e-2); fp32 master / m / v (about 1 MB: launch-bound)",
@@ -473,7 +474,8 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
     lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", "",
               f"Calibration: torch's 2 GiB device copy reads FETCH_SIZE {fetch_cal:.0f} KiB and WRITE_SIZE "
               f"{write_cal:.0f} KiB against 2097152 KiB each: factors {f_fac:.4f} (fetch), {w_fac:.4f} (write).", "",
-              "| kernel | dispatches | avg FETCH KiB | avg WRITE KiB | scaled bytes / dispatch |", "|---|---|---|---|---|"]
+              "| kernel | dispatches | avg FETCH KiB | avg WRITE KiB | scaled bytes / dispatch |",
+              "|---|---|---|---|---|"]
     src_hash = kernel_source_hash()
     for kname, vals in counters["FETCH_SIZE"].items():
         short = _short(kname)

@@ -15,7 +15,8 @@ from ._binding import (EXPORTS, LIB_PATH, LOSS_SCALER_BYTES, ZERO_BF16, ZERO_EHI
 from .step import ShardStep, Zero3Schedule
 
 __all__ = ["EXPORTS", "LIB_PATH", "LOSS_SCALER_BYTES", "Plan", "ShardStep", "Zero3Schedule", "ZeroError", "lib",
-           "ptr_table", "read_loss_scaler", "zero_adam_prepare", "zero_adam_step", "zero_bucket_info", "zero_last_error",
+           "ptr_table", "read_loss_scaler", "zero_adam_prepare", "zero_adam_step", "zero_bucket_info",
+           "zero_last_error",
            "zero_loss_scaler", "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_model_state_bytes",
            "zero_overflow_check", "zero_pack_bucket", "zero_pack_bucket_check", "zero_param_info",
            "zero_plan_bucket_info", "zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy",

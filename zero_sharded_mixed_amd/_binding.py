@@ -21,11 +21,11 @@ ZERO_BF16, ZERO_FP16 = 1, 2
 STATUS_NAMES = {0: "ZERO_OK", -1: "ZERO_EINVAL", -2: "ZERO_ENOMEM", -3: "ZERO_EHIP", -4: "ZERO_ERANGE"}
 
 # Every symbol the header declares (checked against the header by the ABI test).
-EXPORTS = ("zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy", "zero_plan_get_summary", "zero_plan_param_info",
-           "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes", "zero_pack_bucket",
-           "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack", "zero_shard_init",
-           "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket", "zero_loss_scaler_init",
-           "zero_loss_scaler_update", "zero_last_error")
+EXPORTS = ("zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy", "zero_plan_get_summary",
+           "zero_plan_param_info", "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes",
+           "zero_pack_bucket", "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack",
+           "zero_shard_init", "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket",
+           "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_last_error")
 
 
 class ZeroError(RuntimeError):

@@ -1,11 +1,13 @@
-"""One rank's shard step, driven through the C ABI: pack -> reduce (+ overflow flag) -> Adam
--> unpack (or pack with the input check -> fused reduce + Adam -> unpack), the order of the ZeRO-1 sequence on the briefia.fr page ("ZeRO-1 : Partitionnement
-des états de l'optimiseur": gradients synchronised, own partition stepped, parameters
-all-gathered) with the ZeRO-2 reduce-scatter of the ColossalAI "low level zero" issue (BWD).
+"""One rank's shard step, driven through the C ABI: pack -> reduce (+ overflow flag) -> Adam ->
+unpack (or pack with the input check -> fused reduce + Adam -> unpack), the order of the ZeRO-1
+sequence on the briefia.fr page ("ZeRO-1 : Partitionnement des états de l'optimiseur": gradients
+synchronised, own partition stepped, parameters all-gathered) with the ZeRO-2 reduce-scatter of
+the ColossalAI "low level zero" issue (BWD).
 
 This class only allocates the rank's device buffers (sizes read from the plan) and issues the
 entry points in order on one stream; every element of work runs in the HIP kernels.
-"""
+Zero3Schedule issues ZeRO-3's per-layer gathers and reduce-scatters over a plan with one bucket
+per layer."""
 from __future__ import annotations
 
 from typing import Callable, Optional, Sequence
