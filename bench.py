@@ -71,7 +71,15 @@ def algorithmic_bytes(numels, shard_sizes, live, nd):
         "unpack": 4 * numel_all,
         "shard_live": shard_live,
         "numel_live": numel_live,
+        "numel_all": numel_all,
     }
+
+
+def stage_elements(ab):
+    """Elements each stage processes per step: pack the live gradients' elements; reduce,
+    Adam and the fused reduce + Adam the live shard elements; unpack every parameter element."""
+    return {"pack": ab["numel_live"], "reduce": ab["shard_live"], "adam": ab["shard_live"],
+            "reduce_adam": ab["shard_live"], "unpack": ab["numel_all"]}
 
 
 def kernel_source_hash() -> str:
@@ -538,6 +546,7 @@ def main():
     shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
     live = W.live_mask(w, 0)
     ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
+    ne = stage_elements(ab)
     runs = {}
     for path in ("unfused", "fused"):
         ms_p, per_phase, launches, flag = run_gpu(w, ctx, path, args.steps, args.warmup)
@@ -545,7 +554,8 @@ def main():
         for p in PHASES[path]:
             kernels[p] = {"ms": round(per_phase[p], 4), "launches": launches[p], "bytes": ab[p],
                           "GBs": round(ab[p] / (per_phase[p] * 1e-3) / 1e9, 1),
-                          "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                          "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "elements": ne[p], "elem_per_s": round(ne[p] / (per_phase[p] * 1e-3), 1)}
         runs[path] = dict(ms=ms_p, kernels=kernels, launches=launches, flag=flag,
                           bytes=sum(ab[p] for p in PHASES[path]))
     ms, kernels, launches, flag = (runs["unfused"][k] for k in ("ms", "kernels", "launches", "flag"))
