@@ -264,6 +264,37 @@ def run_gpu(w, ctx, path, steps, warmup):
     return wall / steps * 1e3, per_phase, {p: launches[p] for p in phases}, flag
 
 
+def run_graph(w, ctx, steps, warmup):
+    """The unfused step captured once into a HIP graph (torch.cuda.graph) and replayed: the hot
+    calls allocate nothing, never synchronise and clear the flag with a fill kernel, not a
+    memset, so the whole step is one graph launch.  Every buffer the captured kernels touch,
+    through pointer tables included, stays referenced for the life of the graph."""
+    st, own_ptrs, own_out, rows_of, lp, lp_ptrs, live = ctx
+    b1, b2 = w.betas
+
+    def step():
+        st.flag.zero_()
+        st.pack(own_ptrs, out=own_out)
+        st.reduce(rows_of, fused_check=True)
+        st.adam(w.lr, b1, b2, w.eps, w.grad_scale)
+        st.unpack(lp_ptrs)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    del g
+    return ms
+
+
 def run_zero3(w, ctx, steps, warmup, device):
     """ZeRO-3's step on the same list with one bucket per layer (workloads.layer_groups): the
     forward pass gathers every layer's parameters (unpack into a scratch buffer), the backward
@@ -525,6 +556,7 @@ def main():
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero3", action="store_true", help="skip the ZeRO-3 (one bucket per layer) leg")
+    ap.add_argument("--no-graph", action="store_true", help="skip the leg that replays the step as a HIP graph")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="reduce rocprofv3 CSVs under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/) to a text summary "
                          "on stdout and profiles/traffic.json, then exit")
@@ -565,6 +597,11 @@ def main():
              "GBs": round(fz["bytes"] / (fz["ms"] * 1e-3) / 1e9, 1), "step_bytes": fz["bytes"],
              "elem_per_s": round(ab["shard_live"] / (fz["ms"] * 1e-3), 1), "overflow_flag": fz["flag"],
              "kernels": fz["kernels"]}
+    graph = None
+    if not args.no_graph:
+        graph_ms = run_graph(w, ctx, args.steps, args.warmup)
+        graph = {"ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(ms, 4),
+                 "speedup": round(ms / graph_ms, 3)}
     zero3 = None
     if w.emulation == "full" and not args.no_zero3:
         zero3 = run_zero3(w, ctx, args.steps, args.warmup, device)
@@ -604,6 +641,7 @@ def main():
         "kernels": kernels,
         "fused": fused,
         "zero3": zero3,
+        "graph": graph,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["bytes"] / launches[dom] /
                                                                       (d["ms"] / launches[dom] * 1e-3) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],

@@ -164,3 +164,27 @@ def test_accounting_matches_oracle(L, psi, nd):
     assert L.zero_model_state_bytes(psi, nd, 4, ctypes.byref(out)) == B.ZERO_EINVAL
     assert L.zero_model_state_bytes(psi, 0.5, 1, ctypes.byref(out)) == B.ZERO_EINVAL
     assert L.zero_model_state_bytes(-1.0, nd, 1, ctypes.byref(out)) == B.ZERO_EINVAL
+
+
+def test_ptr_table_keeps_its_targets_alive(monkeypatch):
+    """A pointer table must keep the tensors it points at allocated: a table that outlives
+    them would send kernels (or a replayed graph) into freed memory.  Checked on CPU tensors,
+    with the device check of the pointer helper stubbed out."""
+    import gc
+    import weakref
+
+    import torch
+
+    from zero_sharded_mixed_amd import _binding as B
+
+    monkeypatch.setattr(B, "_ptr", lambda t: None if t is None else t.data_ptr())
+    a, b = torch.zeros(16, dtype=torch.int16), torch.ones(8, dtype=torch.int16)
+    wa, wb = weakref.ref(a), weakref.ref(b)
+    table = B.ptr_table([a, None, b], device="cpu")
+    assert table.tolist() == [a.data_ptr(), 0, b.data_ptr()]
+    del a, b
+    gc.collect()
+    assert wa() is not None and wb() is not None
+    del table
+    gc.collect()
+    assert wa() is None and wb() is None

@@ -1,9 +1,12 @@
 """The hot calls inside a HIP graph: they allocate nothing, never synchronise and clear nothing
 with a memset (the flag is cleared by a fill kernel), so one whole step — pack, reduce with
 the fused check, Adam, unpack, or the fused path — can be captured and replayed.  Each replay,
-with eager work and synchronisations between replays, must leave exactly the state the same
-number of eager steps leaves."""
-import numpy as np
+with eager work, synchronisations and a release of the allocator's cache between replays, must
+leave exactly the state the same number of eager steps leaves.
+
+This rank's gradients are reachable only through their pointer table, as in a caller that
+keeps the table and drops its own list: the table holds the tensors, so releasing the cache
+(which torch.cuda.graph also does when capture begins) cannot unmap memory a replay reads."""
 import pytest
 import torch
 
@@ -11,40 +14,52 @@ import workloads as W
 import zero_sharded_mixed_amd as Z
 from gpu_harness import DEV, say
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skip(reason="graph capture is switched off: a benchmark run that replayed a captured "
-                                      "step of the GPT-2 1.5B-shaped list ended in a GPU memory fault whose cause "
-                                      "has not been found; these MlpModel-sized replays passed, but share the "
-                                      "mechanism")]
+pytestmark = pytest.mark.gpu
+
+_SETUPS = {}
 
 
-def mlp_setup():
-    w = W.workload(1)
+def setup_workload(cfg):
+    """MlpModel (one bucket) or the GPT-2 1.5B-shaped list (four 500M-element buckets), full
+    emulation: every virtual rank's gradients packed into its own rows beforehand."""
+    if cfg in _SETUPS:
+        return _SETUPS[cfg]
+    w = W.workload(cfg)
+    say(f"graph setup: {w.name}, Nd={w.nd}, rank {w.rank}")
     st = Z.ShardStep(w.numels, w.nd, w.rank, w.bucket_bytes, w.dtype)
-    masters = [m.to(DEV) for m in W.masters(w, "cpu")]
+    masters = W.masters(w, DEV)
     st.init_master(Z.ptr_table(masters), 0)
     lp = [m.to(torch.bfloat16) for m in masters]
+    del masters
     lp_ptrs = Z.ptr_table(lp)
     st.pack(lp_ptrs, out=st.arena)
     live = W.live_mask(w, 0)
     st.live.copy_(torch.from_numpy(live))
     rows = torch.zeros((w.nd, int(st.summary.arena_numel)), dtype=torch.int16, device=DEV)
-    own = None
+    own_ptrs = None
     for k in range(w.nd):
-        g = [t.to(DEV) if l else None for t, l in zip(W.grads(w, 0, k, "cpu"), live)]
-        st.pack(Z.ptr_table(g), out=rows[k])
+        table = Z.ptr_table([t if l else None for t, l in zip(W.grads(w, 0, k, DEV), live)])
+        st.pack(table, out=rows[k])
         if k == w.rank:
-            own = g
-    return w, st, lp, lp_ptrs, Z.ptr_table(own), rows, own
+            own_ptrs = table  # the only reference to this rank's gradients
+    torch.cuda.synchronize()
+    _SETUPS[cfg] = (w, st, lp, lp_ptrs, own_ptrs, rows)
+    return _SETUPS[cfg]
 
 
-def state_of(st, lp):
-    return [t.clone() for t in (st.p32, st.m, st.v, st.steps, st.arena, st.flag)] + [t.clone() for t in lp]
+def buffers(st, lp):
+    return [st.p32, st.m, st.v, st.steps, st.arena, st.flag] + lp
 
 
+def snapshot(st, lp):
+    return [t.clone() for t in buffers(st, lp)]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg", [1, 2])
 @pytest.mark.parametrize("path", ["unfused", "fused"])
-def test_captured_step_replays_like_eager_steps(path):
-    w, st, lp, lp_ptrs, own_ptrs, rows, own = mlp_setup()
+def test_captured_step_replays_like_eager_steps(cfg, path):
+    w, st, lp, lp_ptrs, own_ptrs, rows = setup_workload(cfg)
     flat = rows.view(-1)
     stride = rows.shape[1]
     r = w.rank
@@ -66,27 +81,36 @@ def test_captured_step_replays_like_eager_steps(path):
             st.reduce_adam(rows_of, *hp)
         st.unpack(lp_ptrs)
 
-    start = state_of(st, lp)
+    start = snapshot(st, lp)
     eager = []
     for _ in range(3):
         step()
         torch.cuda.synchronize()
-        eager.append(state_of(st, lp))
+        eager.append(snapshot(st, lp))
+    assert not torch.equal(eager[0][0], start[0])  # the step moves p32
     # back to the starting state, then capture one step (capture runs nothing)
-    for t, s0 in zip([st.p32, st.m, st.v, st.steps, st.arena, st.flag] + lp, start):
+    for t, s0 in zip(buffers(st, lp), start):
         t.copy_(s0)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):  # torch's capture stream is the current stream inside
         step()
     torch.cuda.synchronize()
-    for t, s0 in zip([st.p32, st.m, st.v, st.steps, st.arena, st.flag] + lp, start):
+    for t, s0 in zip(buffers(st, lp), start):
         assert torch.equal(t, s0)  # capturing executed nothing
     for i in range(3):
+        torch.cuda.empty_cache()
         g.replay()
         torch.cuda.synchronize()
         _ = (st.p32 * 2).sum().item()  # eager work between replays
-        got = state_of(st, lp)
-        for a, b in zip(got, eager[i]):
-            assert torch.equal(a, b), (path, i)
-        say(f"{path}: replay {i} matches eager step {i}")
+        for j, (a, b) in enumerate(zip(buffers(st, lp), eager[i])):
+            assert torch.equal(a, b), (cfg, path, i, j)
+        say(f"{w.name} {path}: replay {i} matches eager step {i}")
+    del g, start, eager
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _release():
+    yield
+    _SETUPS.clear()
+    torch.cuda.empty_cache()

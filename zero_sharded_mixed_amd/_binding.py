@@ -128,9 +128,18 @@ def _stream(stream) -> Optional[int]:
 
 
 def ptr_table(tensors: Sequence[Optional[torch.Tensor]], device=None) -> torch.Tensor:
-    """Device int64 array of the tensors' data pointers (0 for None): a pointer table."""
-    ptrs = [0 if t is None else _ptr(t) for t in tensors]
-    return torch.tensor(ptrs, dtype=torch.int64, device=device or "cuda")
+    """Device int64 array of the tensors' data pointers (0 for None): a pointer table.
+
+    The returned tensor holds references to the tensors it points at (attribute
+    `zero_targets`), so their memory stays allocated for as long as the table object is alive:
+    a kernel that reads through the table, at once or when a captured graph is replayed, never
+    reads memory that the caching allocator has freed or handed back to the driver.  A slice or
+    copy of the table is a new tensor object and does not carry the references."""
+    keep = list(tensors)
+    ptrs = [0 if t is None else _ptr(t) for t in keep]
+    table = torch.tensor(ptrs, dtype=torch.int64, device=device or "cuda")
+    table.zero_targets = keep
+    return table
 
 
 class Plan:
