@@ -295,13 +295,16 @@ def run_graph(w, ctx, steps, warmup):
     return ms
 
 
-def run_zero3(w, ctx, steps, warmup, device):
+def run_zero3(w, ctx, steps, warmup, device, graph=True):
     """ZeRO-3's step on the same list with one bucket per layer (workloads.layer_groups): the
     forward pass gathers every layer's parameters (unpack into a scratch buffer), the backward
     pass gathers all but the last layer again and reduce-scatters each layer's gradients (pack
     + reduce) right after it, then Adam writes this rank's 16-bit shard.  Full emulation: every
     virtual rank's gradients are packed for the per-layer buckets beforehand; this rank's are
-    re-packed inside each timed step, into the rows the reduce reads."""
+    re-packed inside each timed step, into the rows the reduce reads.  Timed twice: all on one
+    stream, and with prefetch (the gathers on a second stream into two scratch buffers, the
+    next layer's gather overlapping the current layer's pack and reduce).  With graph=True each
+    step (about 200 launches) is also captured once into a HIP graph and the replays timed."""
     import workloads as W
 
     st2, own_ptrs, _, _, lp, lp_ptrs, live = ctx
@@ -325,51 +328,77 @@ def run_zero3(w, ctx, steps, warmup, device):
         bk = z.buckets[b]
         return flat[bk.block_offset + w.rank * bk.row_stride:], an
 
+    shard_sizes = [Z.zero_plan_param_info(z.plan, i).shard_size for i in range(z.n)]
+    ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
+    numel_all = int(sum(int(x) for x in w.numels))
+    b1, b2 = w.betas
+    phases = ("forward", "backward", "adam")
+
+    def measure(z3):
+        def one_step(ev=None):
+            def mark(j):
+                if ev is not None:
+                    ev[j].record()
+
+            mark(0)
+            z.flag.zero_()
+            z3.order.clear()
+            z3.forward()
+            mark(1)
+            z3.backward(lambda lid: own_ptrs, rows_of, out=packed_all[w.rank])
+            mark(2)
+            z.adam(w.lr, b1, b2, w.eps, w.grad_scale)
+            mark(3)
+
+        for _ in range(warmup):
+            one_step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
+        t1 = time.perf_counter()
+        for i in range(steps):
+            one_step(events[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t1) / steps * 1e3
+        per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j, p in enumerate(phases)}
+        numel_last = int(sum(int(w.numels[i]) for i in z3.layers[-1]))
+        nbytes = {"forward": 4 * numel_all, "backward": 4 * (numel_all - numel_last) + ab["pack"] + ab["reduce"],
+                  "adam": ab["adam"]}
+        total = sum(nbytes.values())
+        res = {"ms_per_step": round(wall, 4), "GBs": round(total / (wall * 1e-3) / 1e9, 1), "step_bytes": total,
+               "elem_per_s": round(ab["shard_live"] / (wall * 1e-3), 1), "layers": len(z.buckets),
+               "gathers_per_step": len(z3.order), "scratch_elems": int(z3.scratch.numel()),
+               "overflow_flag": int(z.flag.item()),
+               "phases": {p: {"ms": round(per[p], 4), "bytes": nbytes[p],
+                              "GBs": round(nbytes[p] / (per[p] * 1e-3) / 1e9, 1)} for p in phases}}
+        if graph:
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_step()
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            gms = (time.perf_counter() - t1) / steps * 1e3
+            res["graph"] = {"ms_per_step": round(gms, 4), "GBs": round(total / (gms * 1e-3) / 1e9, 1),
+                            "speedup": round(wall / gms, 3)}
+            del g
+        return res
+
     z3 = Z.Zero3Schedule(z)
     torch.cuda.synchronize()
     log(f"[bench] zero3: {len(z.buckets)} layer buckets, scratch {z3.scratch.numel()} elements "
         f"({time.time() - t0:.1f}s)")
-    b1, b2 = w.betas
-    phases = ("forward", "backward", "adam")
-
-    def one_step(ev=None):
-        def mark(j):
-            if ev is not None:
-                ev[j].record()
-
-        mark(0)
-        z.flag.zero_()
-        z3.order.clear()
-        z3.forward()
-        mark(1)
-        z3.backward(lambda lid: own_ptrs, rows_of, out=packed_all[w.rank])
-        mark(2)
-        z.adam(w.lr, b1, b2, w.eps, w.grad_scale)
-        mark(3)
-
-    for _ in range(warmup):
-        one_step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
-    t1 = time.perf_counter()
-    for i in range(steps):
-        one_step(events[i])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t1) / steps * 1e3
-    per = {p: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / steps for j, p in enumerate(phases)}
-    shard_sizes = [Z.zero_plan_param_info(z.plan, i).shard_size for i in range(z.n)]
-    ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
-    numel_all = int(sum(int(x) for x in w.numels))
-    last = z3.layers[-1]
-    numel_last = int(sum(int(w.numels[i]) for i in last))
-    nbytes = {"forward": 4 * numel_all, "backward": 4 * (numel_all - numel_last) + ab["pack"] + ab["reduce"],
-              "adam": ab["adam"]}
-    total = sum(nbytes.values())
-    out = {"ms_per_step": round(wall, 4), "GBs": round(total / (wall * 1e-3) / 1e9, 1), "step_bytes": total,
-           "elem_per_s": round(ab["shard_live"] / (wall * 1e-3), 1), "layers": len(z.buckets),
-           "gathers_per_step": len(z3.order), "overflow_flag": int(z.flag.item()),
-           "phases": {p: {"ms": round(per[p], 4), "bytes": nbytes[p],
-                          "GBs": round(nbytes[p] / (per[p] * 1e-3) / 1e9, 1)} for p in phases}}
+    out = measure(z3)
+    del z3
+    # the same step with the gathers on a second stream into two scratch buffers
+    z3 = Z.Zero3Schedule(z, prefetch=True)
+    pf = measure(z3)
+    pf["speedup"] = round(out["ms_per_step"] / pf["ms_per_step"], 3)
+    out["prefetch"] = pf
     del packed_all, z3, z
     torch.cuda.empty_cache()
     return out
@@ -604,7 +633,7 @@ def main():
                  "speedup": round(ms / graph_ms, 3)}
     zero3 = None
     if w.emulation == "full" and not args.no_zero3:
-        zero3 = run_zero3(w, ctx, args.steps, args.warmup, device)
+        zero3 = run_zero3(w, ctx, args.steps, args.warmup, device, graph=not args.no_graph)
     fk = fz["kernels"]["reduce_adam"]
     fused["roofline"] = {"bound": "hbm", "kernel": "reduce_adam", "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "achieved": fk["GBs"], "frac": fk["frac"],

@@ -50,8 +50,9 @@ def test_grouped_plan_tables(nd, cap, seed):
         assert np.all(members == members[0])  # a bucket never spans two runs of ids
 
 
+@pytest.mark.parametrize("prefetch", [False, True])
 @pytest.mark.parametrize("nd,rank,dtype", [(8, 3, BF16), (64, 17, FP16)])
-def test_zero3_step_matches_oracle(nd, rank, dtype):
+def test_zero3_step_matches_oracle(nd, rank, dtype, prefetch):
     n_layers, d, vocab = 3, 48, 500
     numels, groups = layered_model(n_layers, d, vocab)
     say(f"zero3 nd={nd} rank={rank} layers={n_layers + 2}")
@@ -74,7 +75,7 @@ def test_zero3_step_matches_oracle(nd, rank, dtype):
     live = np.ones(len(numels), np.uint8)
     live[[3, 4]] = 0  # two parameters of layer 1 without a gradient (the layer-drop mapping)
     st.live.copy_(torch.from_numpy(live))
-    z3 = Z.Zero3Schedule(st)
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch)
 
     def check_gather(lid, params):
         outs = [np.zeros(x, np.uint16) for x in numels]
@@ -115,13 +116,16 @@ def test_zero3_step_matches_oracle(nd, rank, dtype):
     # model states at stage 3 against the accounting of the ZeRO summary (16 Psi / Nd)
     psi = float(pl.params[:, oracle.P_PADDED].sum())
     assert Z.zero_plan_model_state_bytes(st.plan, 3) == pytest.approx(16 * psi / nd)
-    # at most one layer's full parameters at a time: the scratch holds the largest layer
+    # at most one layer's full parameters at a time (two with prefetch): each scratch buffer
+    # holds the largest layer
     biggest = max(sum(numels[i] for i in z3.layers[b]) for b in range(pl.n_buckets))
-    assert biggest <= z3.scratch.numel() < biggest + 8 * 8
+    assert biggest <= z3.buffer_numel < biggest + 8 * 8
+    assert z3.scratch.numel() == (2 if prefetch else 1) * z3.buffer_numel
 
 
 @pytest.mark.timeout(900)
-def test_zero3_fullsize_gpt2_matches_zero2_and_oracle():
+@pytest.mark.parametrize("prefetch", [False, True])
+def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(prefetch):
     """The GPT-2 1.5B-shaped list at Nd = 8 with one bucket per layer, as bench.py's ZeRO-3 leg
     runs it: every forward gather restores its layer's parameters exactly; after the step,
     p32 / m / v and this rank's 16-bit shard equal the ZeRO-2 step's (same gradients, 500M-element
@@ -167,7 +171,7 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle():
     hp = (w.lr, w.betas[0], w.betas[1], w.eps, w.grad_scale)
     A.adam(*hp)
     # ZeRO-3
-    z3 = Z.Zero3Schedule(G)
+    z3 = Z.Zero3Schedule(G, prefetch=prefetch)
 
     def restored(lid, params):
         for i, view in zip(z3.layers[lid], params):

@@ -127,11 +127,22 @@ class Zero3Schedule:
     gradients are reduce-scattered (pack + reduce) as soon as its backward has run.
 
     The gather of layer l is zero_unpack of bucket l from the all-gather block (the Nd ranks'
-    rows of that layer); its destination is one scratch buffer sized for the largest layer, so
-    at most one layer's full parameters exist at a time."""
+    rows of that layer).  Without prefetch its destination is one scratch buffer sized for the
+    largest layer, so at most one layer's full parameters exist at a time, and everything runs
+    in order on the caller's stream.
 
-    def __init__(self, st: ShardStep):
+    With prefetch=True the gathers run on a second stream into two scratch buffers (layer l in
+    buffer l % 2), so the gather of the next layer overlaps the use of the current one and, in
+    the backward pass, its pack and reduce.  Events order the two streams: a gather waits until
+    the caller's stream has finished using the buffer's previous layer, a layer's use waits
+    for its gather, and each pass starts by waiting for the caller's stream (Adam's writes to
+    the all-gather block included) and ends with the caller's stream waiting for the gathers,
+    so a pass can also be captured into a graph.  At most two layers' parameters exist at a
+    time.  `use` callbacks run with the caller's stream current."""
+
+    def __init__(self, st: ShardStep, prefetch: bool = False):
         self.st = st
+        self.prefetch = prefetch
         nb = len(st.buckets)
         infos = [B.zero_plan_param_info(st.plan, i) for i in range(st.n)]
         self.layers = [list(range(int(bk.first_param), int(bk.first_param + bk.n_params))) for bk in st.buckets]
@@ -139,10 +150,13 @@ class Zero3Schedule:
         biggest = max((sum(x) for x in self.numel), default=0)
         # each parameter 16-byte aligned inside the scratch (the unpack's wide path)
         per = [sum((x + 7) // 8 * 8 for x in xs) for xs in self.numel]
-        self.scratch = torch.zeros(max(per + [biggest, 8]), dtype=torch.int16, device=st.device)
+        need = max(per + [biggest, 8])
+        nbuf = 2 if prefetch else 1
+        self.buffer_numel = need
+        self.scratch = torch.zeros(nbuf * need, dtype=torch.int16, device=st.device)
         self.views, self.tables = [], []
         for lid in range(nb):
-            views, pos = [], 0
+            views, pos = [], (lid % nbuf) * need
             for x in self.numel[lid]:
                 views.append(self.scratch[pos:pos + x])
                 pos += (x + 7) // 8 * 8
@@ -152,21 +166,69 @@ class Zero3Schedule:
             self.views.append(views)
             self.tables.append(B.ptr_table(full, device=st.device))
         self.order: list = []  # layers in the order they were gathered
+        if prefetch:
+            self.side = torch.cuda.Stream(device=st.device)
+            self.ready = [torch.cuda.Event() for _ in range(nb)]
+            self.free = [torch.cuda.Event(), torch.cuda.Event()]
+            self.fork_ev, self.join_ev = torch.cuda.Event(), torch.cuda.Event()
 
     def gather(self, lid: int, src: Optional[torch.Tensor] = None, stream=None) -> list:
-        """All-gather layer lid's parameters (the unpack of its bucket) into the scratch buffer;
-        returns one view per parameter, valid until the next gather."""
+        """All-gather layer lid's parameters (the unpack of its bucket) into its scratch buffer;
+        returns one view per parameter, valid until that buffer's next gather."""
         st = self.st
         src = st.arena if src is None else src
         B.zero_unpack(st.plan, lid, st.block(src, lid), self.tables[lid], stream)
         self.order.append(lid)
         return self.views[lid]
 
+    # -- two-stream helpers (prefetch) -------------------------------------------------------
+
+    def _main(self, stream) -> torch.cuda.Stream:
+        if stream is None:
+            return torch.cuda.current_stream(self.st.device)
+        if isinstance(stream, torch.cuda.Stream):
+            return stream
+        return torch.cuda.ExternalStream(int(stream), device=self.st.device)
+
+    def _fork(self, main) -> None:
+        self.fork_ev.record(main)
+        self.side.wait_event(self.fork_ev)
+        self._recorded = [False, False]  # free[b] recorded in this pass
+
+    def _join(self, main) -> None:
+        self.join_ev.record(self.side)
+        main.wait_event(self.join_ev)
+
+    def _gather_side(self, lid: int) -> None:
+        buf = lid % 2
+        if self._recorded[buf]:
+            self.side.wait_event(self.free[buf])  # the buffer's previous layer is no longer used
+        self.gather(lid, stream=self.side)
+        self.ready[lid].record(self.side)
+
+    def _use(self, main, lid: int, use) -> None:
+        if use is not None:
+            with torch.cuda.stream(main):
+                use(lid, self.views[lid])
+        self.free[lid % 2].record(main)
+        self._recorded[lid % 2] = True
+
+    # -- passes --------------------------------------------------------------------------------
+
     def forward(self, use: Optional[Callable[[int, list], None]] = None, stream=None) -> None:
+        if not self.prefetch:
+            for lid in range(len(self.layers)):
+                params = self.gather(lid, stream=stream)
+                if use is not None:
+                    use(lid, params)
+            return
+        main = self._main(stream)
+        self._fork(main)
         for lid in range(len(self.layers)):
-            params = self.gather(lid, stream=stream)
-            if use is not None:
-                use(lid, params)
+            self._gather_side(lid)
+            main.wait_event(self.ready[lid])
+            self._use(main, lid, use)
+        self._join(main)
 
     def backward(self, grads_of: Callable[[int], torch.Tensor], rows_of: Callable[[int], tuple],
                  use: Optional[Callable[[int, list], None]] = None, check: bool = False,
@@ -177,13 +239,25 @@ class Zero3Schedule:
         st = self.st
         out = st.packed if out is None else out
         last = len(self.layers) - 1
+        main = self._main(stream) if self.prefetch else stream
+        if self.prefetch:
+            self._fork(main)  # the last layer is still in its buffer from the forward pass
         for lid in range(last, -1, -1):
-            params = self.views[lid] if lid == last else self.gather(lid, stream=stream)
-            if use is not None:
-                use(lid, params)
-            if check:
-                B.zero_pack_bucket_check(st.plan, lid, grads_of(lid), st.block(out, lid), st.flag, stream)
+            if not self.prefetch:
+                params = self.views[lid] if lid == last else self.gather(lid, stream=stream)
+                if use is not None:
+                    use(lid, params)
             else:
-                B.zero_pack_bucket(st.plan, lid, grads_of(lid), st.block(out, lid), stream)
+                if lid != last:
+                    main.wait_event(self.ready[lid])
+                if lid > 0:
+                    self._gather_side(lid - 1)  # the next layer's gather overlaps this layer's work
+                self._use(main, lid, use)
+            if check:
+                B.zero_pack_bucket_check(st.plan, lid, grads_of(lid), st.block(out, lid), st.flag, main)
+            else:
+                B.zero_pack_bucket(st.plan, lid, grads_of(lid), st.block(out, lid), main)
             rows, stride = rows_of(lid)
-            B.zero_reduce_shard(st.plan, lid, rows, stride, st.live, st.g32, st.flag, stream)
+            B.zero_reduce_shard(st.plan, lid, rows, stride, st.live, st.g32, st.flag, main)
+        if self.prefetch:
+            self._join(main)
