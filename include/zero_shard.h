@@ -52,6 +52,14 @@
  *   zero_last_error() returns a thread-local message for the last failing call.
  *   A plan stays valid after any failed hot call.
  *
+ * Empty work:
+ *   A call with nothing to move -- a per-bucket call on a bucket whose rows are empty
+ *   (L_b = 0: only parameters of numel 0), or a shard-wide call on a plan whose shard has no
+ *   elements -- checks the plan and the bucket index and returns ZERO_OK; its buffer pointers
+ *   may then be NULL (a zero-length tensor often has a NULL data pointer).  zero_adam_step on
+ *   an empty shard still advances the step counts of live parameters, so it still needs
+ *   d_live, d_steps and hp.
+ *
  * Alignment:
  *   Block buffers (packed, gathered, all-gather arena, receive rows) and the fp32 shard
  *   arrays must be 16-byte aligned (ZERO_EINVAL otherwise).  Per-parameter gradient and

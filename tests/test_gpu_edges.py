@@ -185,3 +185,67 @@ def test_repeated_runs_are_bit_identical():
                      np.concatenate([to_np16(p) for p in params])])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_empty_buckets_and_shards_take_null_buffers():
+    """A bucket holding only empty parameters (here closed off by a one-element capacity) has
+    empty rows; its block is a zero-length tensor whose data pointer is NULL.  Every per-bucket
+    call accepts that and does nothing, and the whole step runs through ShardStep, unfused and
+    fused, with the other buckets matching the oracle.  A model of only empty parameters runs
+    every call with NULL shard buffers."""
+    numels, nd, rank = [100, 0, 0, 50], 4, 1
+    st = Z.ShardStep(numels, nd, rank, 2, BF16)
+    pl = oracle.plan(numels, nd, rank, 2)
+    assert [int(bk.row_stride) for bk in st.buckets] == [32, 0, 16]  # the two empty ones share a bucket
+    assert st.block(st.packed, 1).numel() == 0
+    L_ = B.lib()
+    for b in (1,):  # NULL buffers on an empty bucket: nothing to do, no error
+        assert L_.zero_pack_bucket(st.plan.handle, b, None, None, None) == B.ZERO_OK
+        assert L_.zero_pack_bucket_check(st.plan.handle, b, None, None, None, None) == B.ZERO_OK
+        assert L_.zero_unpack(st.plan.handle, b, None, None, None) == B.ZERO_OK
+        assert L_.zero_reduce_shard(st.plan.handle, b, None, 0, None, None, None, None) == B.ZERO_OK
+        assert L_.zero_reduce_adam_bucket(st.plan.handle, b, None, 0, None, None, None, None, None, None,
+                                          None) == B.ZERO_OK
+    rng = np.random.default_rng(12)
+    grads = [(rng.standard_normal(x) * 1e-2).astype(np.float32) for x in numels]
+    g16 = [torch.from_numpy(g).to(torch.bfloat16).to(DEV) for g in grads]
+    host = [to_np16(t) for t in g16]
+    st.pack(Z.ptr_table(g16))
+    want = np.zeros(int(st.summary.arena_numel), np.uint16)
+    for b in range(pl.n_buckets):
+        L = int(pl.buckets[b, oracle.B_STRIDE])
+        if L:
+            off = nd * int(pl.buckets[b, oracle.B_BASE])
+            want[off:off + nd * L] = oracle.pack_bucket(pl, b, host).reshape(-1)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np16(st.packed), want)
+    F = Z.ShardStep(numels, nd, rank, 2, BF16)
+    F.pack(Z.ptr_table(g16), check=True)
+    rows_of = lambda b: (st.block(st.packed, b), int(st.buckets[b].row_stride))  # noqa: E731
+    st.reduce(rows_of)
+    st.adam(**HP)
+    F.reduce_adam(rows_of, **HP)
+    g32 = np.zeros(pl.shard_len, np.float32)
+    live = np.ones(len(numels), np.uint8)
+    for b in range(pl.n_buckets):
+        L = int(pl.buckets[b, oracle.B_STRIDE])
+        off = nd * int(pl.buckets[b, oracle.B_BASE])
+        oracle.reduce_bucket(pl, b, want[off:off + nd * L].reshape(nd, L), BF16, live, g32)
+    st.unpack(Z.ptr_table(g16))
+    torch.cuda.synchronize()
+    assert_same_f32(to_np32(st.g32), g32, "g32")
+    assert torch.equal(st.p32, F.p32) and torch.equal(st.arena, F.arena)
+    assert torch.all(st.steps == 1) and int(st.flag.item()) == int(F.flag.item()) == 0
+    # a model of only empty parameters: every shard buffer has no elements (NULL pointers)
+    E = Z.ShardStep([0, 0, 0], 8, 5, 0, FP16)
+    assert E.p32.numel() == 0 and E.packed.numel() == 0
+    empty = Z.ptr_table([E.packed] * 3)
+    E.init_master(empty, 0)
+    E.pack(empty, check=True)
+    E.reduce(lambda b: (E.packed, 0))
+    E.overflow_check()
+    E.adam(**HP)
+    E.reduce_adam(lambda b: (E.packed, 0), **HP)
+    E.unpack(empty)
+    torch.cuda.synchronize()
+    assert torch.all(E.steps == 2) and int(E.flag.item()) == 0

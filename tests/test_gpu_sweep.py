@@ -1,0 +1,159 @@
+"""Randomised end-to-end parity through the C ABI: seeded random plans (Nd from 1 to 1031, odd
+ones included; any rank; bucket capacities from one element to one bucket; optional group ids;
+bf16 or fp16; tiny, empty and multi-tile parameters; dead parameters; misaligned per-parameter
+buffers), each run through the whole step on the unfused path — plan tables, pack, Nd-way
+reduce with the fused flag, Adam, unpack — and on the fused path — checked pack, reduce + Adam —
+against the oracle: bit for bit for the plan, pack, reduce, flag and unpack; Adam within its
+tolerance; the fused path bit-identical to the unfused one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_sharded_mixed_amd as Z
+from gpu_harness import (DEV, assert_close_f32, assert_same_f32, check_arena, oracle_block, placed_views,
+                         random_bits, say, to_dev16, to_np16, to_np32)
+
+pytestmark = pytest.mark.gpu
+BF16, FP16 = Z.ZERO_BF16, Z.ZERO_FP16
+SENT16 = 0x5A5A
+NDS = [1, 2, 3, 5, 7, 8, 13, 16, 31, 64, 100, 257, 1024, 1031]
+
+
+def random_case(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    nd = int(rng.choice(NDS))
+    rank = int(rng.integers(0, nd))
+    n = int(rng.integers(1, 120))
+    kinds = rng.choice(4, size=n, p=[0.3, 0.35, 0.3, 0.05])  # few multi-tile parameters
+    numels = []
+    for k in kinds:
+        if k == 0:
+            numels.append(int(rng.integers(0, 2 * nd + 2)))        # empty, below Nd, about Nd
+        elif k == 1:
+            numels.append(int(rng.integers(0, 3000)))
+        elif k == 2:
+            numels.append(int(rng.integers(3000, 40000)))
+        else:
+            numels.append(int(nd * 2048 * int(rng.integers(1, 3)) + int(rng.integers(-3, 4)) * nd
+                              + int(rng.integers(0, nd))))         # whole tiles, ragged tail
+    numels = [max(0, x) for x in numels]
+    total = sum(numels)
+    cap = int(rng.choice([0, 2, 2 * max(1, total // 7), 2 * max(1, total // 2), 2 * int(rng.integers(1, 5000))]))
+    groups = None
+    if rng.random() < 0.4:
+        groups = np.cumsum(rng.random(n) < 0.15).astype(np.int32)
+    dtype = BF16 if rng.random() < 0.5 else FP16
+    return rng, nd, rank, numels, cap, groups, dtype
+
+
+def finite_bits(rng, n, dtype):
+    return random_bits(rng, n) & np.uint16(0xBFFF if dtype == BF16 else 0xBBFF)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_plan_whole_step(seed):
+    rng, nd, rank, numels, cap, groups, dtype = random_case(seed)
+    say(f"sweep seed={seed} nd={nd} rank={rank} n={len(numels)} total={sum(numels)} cap={cap} "
+        f"groups={'yes' if groups is not None else 'no'} dtype={dtype}")
+    gl = None if groups is None else [int(x) for x in groups]
+    A = Z.ShardStep(numels, nd, rank, cap, dtype, groups=gl)   # unfused
+    F = Z.ShardStep(numels, nd, rank, cap, dtype, groups=gl)   # fused
+    pl = oracle.plan(numels, nd, rank, cap, groups)
+    S = pl.shard_len
+    # plan tables
+    assert (A.summary.n_buckets, A.summary.shard_numel) == (pl.n_buckets, S)
+    for i in range(len(numels)):
+        info = Z.zero_plan_param_info(A.plan, i)
+        assert [info.numel, info.pad, info.padded_numel, info.shard_size, info.shard_start, info.shard_end,
+                info.shard_offset, info.bucket, info.bucket_col] == list(pl.params[i]), i
+    for b in range(pl.n_buckets):
+        bk = Z.zero_plan_bucket_info(A.plan, b)
+        assert [bk.first_param, bk.n_params, bk.row_elems, bk.row_stride, bk.shard_base] == list(pl.buckets[b])
+
+    # state: p32 N(0, 0.02), m = v = 0, step counts 0..2, all-gather block of finite patterns
+    p32 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    steps = rng.integers(0, 3, size=len(numels)).astype(np.int32)
+    arena = finite_bits(rng, nd * S, dtype)
+    for X in (A, F):
+        X.p32.copy_(torch.from_numpy(p32))
+        X.steps.copy_(torch.from_numpy(steps))
+        X.arena.copy_(to_dev16(arena))
+    live = (rng.random(len(numels)) > 0.2).astype(np.uint8)
+    for X in (A, F):
+        X.live.copy_(torch.from_numpy(live))
+
+    # this rank's gradients, dead ones absent, at random (mis)alignments
+    grads = [finite_bits(rng, x, dtype) if l else None for x, l in zip(numels, live)]
+    _buf, views = placed_views(grads, rng, misalign=bool(rng.random() < 0.5))
+    ptrs = Z.ptr_table(views)
+    A.packed.fill_(SENT16)
+    A.pack(ptrs)
+    F.packed.fill_(SENT16)
+    F.flag.zero_()
+    F.pack(ptrs, check=True)
+    torch.cuda.synchronize()
+    got_a, got_f = to_np16(A.packed), to_np16(F.packed)
+    assert np.array_equal(got_a, got_f)  # the checked pack writes the same bits
+    want_flag = 0
+    rows = []
+    for b in range(pl.n_buckets):
+        want = np.full((nd, pl.buckets[b, oracle.B_STRIDE]), SENT16, dtype=np.uint16)
+        oracle.pack_bucket(pl, b, grads, out=want)
+        assert np.array_equal(oracle_block(pl, got_a, b), want), f"pack bucket {b}"
+        want_flag |= oracle.input_check(pl, b, grads, dtype)
+        # the Nd ranks' rows r of bucket b: the others random, this rank's from its own pack
+        L = int(pl.buckets[b, oracle.B_STRIDE])
+        r_rows = finite_bits(rng, nd * L, dtype).reshape(nd, L)
+        r_rows[rank] = want[rank]
+        rows.append(r_rows)
+    assert int(F.flag.item()) == want_flag == 0
+    rdev = [to_dev16(r.reshape(-1)) if r.size else torch.zeros(8, dtype=torch.int16, device=DEV) for r in rows]
+
+    def rows_of(b):
+        return rdev[b], int(pl.buckets[b, oracle.B_STRIDE])
+
+    # unfused: reduce (+ flag), Adam
+    A.flag.zero_()
+    A.g32.fill_(-5.0)
+    A.reduce(rows_of)
+    g32 = np.full(S, -5.0, np.float32)
+    for b in range(pl.n_buckets):
+        oracle.reduce_bucket(pl, b, rows[b], dtype, live, g32)
+    torch.cuda.synchronize()
+    assert_same_f32(to_np32(A.g32), g32, "g32")
+    flag = oracle.overflow(pl, g32, live)
+    assert int(A.flag.item()) == flag == 0
+    hp = oracle.AdamHP(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, grad_scale=1.0 / nd)
+    A.adam(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.grad_scale)
+    # fused: reduce + Adam per bucket
+    F.reduce_adam(rows_of, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.grad_scale)
+    oracle.adam(pl, g32, p32, m, v, live, steps, hp, 0, arena, dtype)
+    torch.cuda.synchronize()
+    for ta, tf in ((A.p32, F.p32), (A.m, F.m), (A.v, F.v)):
+        assert torch.equal(ta.view(torch.int32), tf.view(torch.int32))
+    assert torch.equal(A.steps, F.steps) and torch.equal(A.arena, F.arena)
+    assert np.array_equal(to_np32(A.steps), steps)
+    assert_close_f32(to_np32(A.p32), p32, "p32")
+    assert_close_f32(to_np32(A.m), m, "m")
+    assert_close_f32(to_np32(A.v), v, "v", abs_=8 * 2.0 ** -149, rel=2e-6)
+    ever = np.zeros(S, dtype=bool)
+    for i in np.flatnonzero(live):
+        o, s_ = pl.params[i, oracle.P_OFFSET], pl.params[i, oracle.P_SHARD]
+        ever[o:o + s_] = True
+    got_arena = to_np16(A.arena)
+    check_arena(pl, got_arena, arena, to_np32(A.p32), p32, ever, dtype, "arena")
+
+    # unpack the (device) all-gather blocks into fresh, possibly misaligned outputs
+    skip = rng.random(len(numels)) < 0.1
+    outs = [None if sk else np.full(x, SENT16, dtype=np.uint16) for x, sk in zip(numels, skip)]
+    _obuf, oviews = placed_views(outs, rng, misalign=bool(rng.random() < 0.5))
+    A.unpack(Z.ptr_table(oviews))
+    torch.cuda.synchronize()
+    for b in range(pl.n_buckets):
+        oracle.unpack_bucket(pl, b, oracle_block(pl, got_arena, b).copy(), outs)
+    for i, (o, vw) in enumerate(zip(outs, oviews)):
+        if o is not None:
+            assert np.array_equal(to_np16(vw), o), f"unpack param {i}"

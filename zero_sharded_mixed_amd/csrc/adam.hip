@@ -192,7 +192,8 @@ extern "C" zero_status zero_adam_step(const zero_plan* plan, const float* d_g32,
                                       const int32_t* d_flag, void* d_arena, void* stream) {
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
-    if (!d_g32 || !d_p32 || !d_m || !d_v || !d_live || !d_steps || !hp || !d_arena)
+    // an empty shard still advances the step counts of live parameters; its arrays may be NULL
+    if (plan->shard_numel != 0 && (!d_g32 || !d_p32 || !d_m || !d_v || !d_arena))
         return fail(ZERO_EINVAL, "zero_adam_step: NULL pointer");
     if (!host_aligned16(d_g32) || !host_aligned16(d_p32) || !host_aligned16(d_m) || !host_aligned16(d_v) ||
         !host_aligned16(d_arena))

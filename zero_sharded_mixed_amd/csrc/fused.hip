@@ -125,17 +125,17 @@ extern "C" zero_status zero_reduce_adam_bucket(const zero_plan* plan, int64_t b,
     if (st != ZERO_OK) return st;
     if (b < 0 || b >= plan->n_buckets)
         return fail(ZERO_EINVAL, "zero_reduce_adam_bucket: bucket %lld out of range", (long long)b);
+    const int64_t* br = plan->h_bucket + b * kBucketFields;
+    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
+    if (row == 0) return ZERO_OK;  // empty rows: nothing to read or write, buffers may be NULL
     if (!d_rows || !d_live || !d_p32 || !d_m || !d_v || !d_arena)
         return fail(ZERO_EINVAL, "zero_reduce_adam_bucket: NULL pointer");
     if (!host_aligned16(d_rows) || !host_aligned16(d_p32) || !host_aligned16(d_m) || !host_aligned16(d_v) ||
         !host_aligned16(d_arena))
         return fail(ZERO_EINVAL, "zero_reduce_adam_bucket: rows, shard arrays and arena must be 16-byte aligned");
-    const int64_t* br = plan->h_bucket + b * kBucketFields;
-    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
     if (row_stride < stride || row_stride % kChunk != 0)
         return fail(ZERO_EINVAL, "zero_reduce_adam_bucket: row_stride %lld must be >= %lld and a multiple of 8",
                     (long long)row_stride, (long long)stride);
-    if (row == 0) return ZERO_OK;
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
     const int g = grid_for(n_tile);

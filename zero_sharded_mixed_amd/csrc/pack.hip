@@ -415,11 +415,11 @@ static zero_status pack_common(const zero_plan* plan, int64_t b, const void* con
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
     if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "%s: bucket %lld out of range", who, (long long)b);
-    if (!d_grad_ptrs || !d_packed || (check && !d_flag)) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
-    if (!host_aligned16(d_packed)) return fail(ZERO_EINVAL, "%s: packed buffer not 16-byte aligned", who);
     const int64_t* br = bucket_row(plan, b);
     const int64_t base = br[BF_BASE], stride = br[BF_STRIDE];
-    if (stride == 0) return ZERO_OK;
+    if (stride == 0) return ZERO_OK;  // empty rows: nothing to read or write, buffers may be NULL
+    if (!d_grad_ptrs || !d_packed || (check && !d_flag)) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
+    if (!host_aligned16(d_packed)) return fail(ZERO_EINVAL, "%s: packed buffer not 16-byte aligned", who);
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + stride + kTileCols - 1) >> kTileShift) - tile0;
     const int64_t n_rg = (plan->nd + kPackRows - 1) / kPackRows;
@@ -455,11 +455,11 @@ extern "C" zero_status zero_unpack(const zero_plan* plan, int64_t b, const void*
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
     if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "zero_unpack: bucket %lld out of range", (long long)b);
-    if (!d_gathered || !d_param_ptrs) return fail(ZERO_EINVAL, "zero_unpack: NULL pointer");
-    if (!host_aligned16(d_gathered)) return fail(ZERO_EINVAL, "zero_unpack: gathered buffer not 16-byte aligned");
     const int64_t* br = bucket_row(plan, b);
     const int64_t u0 = plan->h_bucket_chunks[2 * b], u1 = plan->h_bucket_chunks[2 * b + 1];
-    if (u1 == u0) return ZERO_OK;
+    if (u1 == u0) return ZERO_OK;  // only empty parameters: nothing to move, buffers may be NULL
+    if (!d_gathered || !d_param_ptrs) return fail(ZERO_EINVAL, "zero_unpack: NULL pointer");
+    if (!host_aligned16(d_gathered)) return fail(ZERO_EINVAL, "zero_unpack: gathered buffer not 16-byte aligned");
     const int64_t n_ut = ((u1 + kUTileChunks - 1) >> kUTileShift) - (u0 >> kUTileShift);
     unpack_kernel<<<grid_for((n_ut + kUnpackUnroll - 1) / kUnpackUnroll), kBlock, 0, (hipStream_t)stream>>>(
         plan->dev, br[BF_BASE], br[BF_STRIDE], u0, u1, static_cast<const uint16_t*>(d_gathered),
@@ -471,9 +471,11 @@ extern "C" zero_status zero_shard_init(const zero_plan* plan, const void* const*
                                        float* d_p32, void* stream) {
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
+    if (src_dtype != 0 && src_dtype != ZERO_BF16 && src_dtype != ZERO_FP16)
+        return fail(ZERO_EINVAL, "zero_shard_init: bad src_dtype %d", src_dtype);
+    if (plan->shard_numel == 0) return ZERO_OK;  // empty shard: buffers may be NULL
     if (!d_src_ptrs || !d_p32) return fail(ZERO_EINVAL, "zero_shard_init: NULL pointer");
     if (!host_aligned16(d_p32)) return fail(ZERO_EINVAL, "zero_shard_init: p32 not 16-byte aligned");
-    if (plan->shard_numel == 0) return ZERO_OK;
     const int g = grid_for(plan->dev.n_tiles);
     hipStream_t s = (hipStream_t)stream;
     switch (src_dtype) {

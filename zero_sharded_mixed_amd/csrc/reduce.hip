@@ -93,15 +93,15 @@ extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
     if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "zero_reduce_shard: bucket %lld out of range", (long long)b);
+    const int64_t* br = plan->h_bucket + b * kBucketFields;
+    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
+    if (row == 0) return ZERO_OK;  // empty rows: nothing to read or write, buffers may be NULL
     if (!d_rows || !d_live || !d_g32) return fail(ZERO_EINVAL, "zero_reduce_shard: NULL pointer");
     if (!host_aligned16(d_rows) || !host_aligned16(d_g32))
         return fail(ZERO_EINVAL, "zero_reduce_shard: rows and g32 must be 16-byte aligned");
-    const int64_t* br = plan->h_bucket + b * kBucketFields;
-    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
     if (row_stride < stride || row_stride % kChunk != 0)
         return fail(ZERO_EINVAL, "zero_reduce_shard: row_stride %lld must be >= %lld and a multiple of 8",
                     (long long)row_stride, (long long)stride);
-    if (row == 0) return ZERO_OK;
     const int64_t tile0 = base >> kTileShift;
     const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
     const int g = grid_for((n_tile + kReduceTiles - 1) / kReduceTiles);
@@ -120,9 +120,9 @@ extern "C" zero_status zero_overflow_check(const zero_plan* plan, const float* d
                                            int32_t* d_flag, void* stream) {
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
+    if (plan->shard_numel == 0) return ZERO_OK;  // empty shard: buffers may be NULL
     if (!d_g32 || !d_live || !d_flag) return fail(ZERO_EINVAL, "zero_overflow_check: NULL pointer");
     if (!host_aligned16(d_g32)) return fail(ZERO_EINVAL, "zero_overflow_check: g32 not 16-byte aligned");
-    if (plan->shard_numel == 0) return ZERO_OK;
     overflow_kernel<<<grid_for(plan->dev.n_tiles), kBlock, 0, (hipStream_t)stream>>>(plan->dev, d_g32, d_live,
                                                                                           d_flag);
     return check_launch("zero_overflow_check");
