@@ -51,7 +51,7 @@ def finite_bits(rng, n, dtype):
     return random_bits(rng, n) & np.uint16(0xBFFF if dtype == BF16 else 0xBBFF)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_plan_whole_step(seed):
     rng, nd, rank, numels, cap, groups, dtype = random_case(seed)
     say(f"sweep seed={seed} nd={nd} rank={rank} n={len(numels)} total={sum(numels)} cap={cap} "
