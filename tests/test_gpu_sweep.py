@@ -157,3 +157,75 @@ def test_random_plan_whole_step(seed):
     for i, (o, vw) in enumerate(zip(outs, oviews)):
         if o is not None:
             assert np.array_equal(to_np16(vw), o), f"unpack param {i}"
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_plan_overflow_skips(seed):
+    """The same random plans with one inf or NaN planted in this rank's own row of a live
+    gradient: the checked pack flags it (the oracle's input check), the unfused reduce flags it
+    (the oracle's overflow of the sums), and both paths then skip the step, leaving p32, m, v, the
+    step counts and the all-gather block bit for bit as they were."""
+    rng, nd, rank, numels, cap, groups, dtype = random_case(seed + 500)
+    pl = oracle.plan(numels, nd, rank, cap, groups)
+    S = pl.shard_len
+    # a live parameter with at least one real element in row `rank`
+    cand = [i for i, x in enumerate(numels) if x > rank * pl.params[i, oracle.P_SHARD]]
+    if not cand:
+        pytest.skip("no parameter has a real element in this rank's row")
+    i = int(rng.choice(cand))
+    s_i = int(pl.params[i, oracle.P_SHARD])
+    j = int(rng.integers(0, min(s_i, numels[i] - rank * s_i)))
+    bad = int(rng.choice([0x7F80, 0xFF80, 0x7FC0] if dtype == BF16 else [0x7C00, 0xFC00, 0x7E00]))
+    say(f"overflow sweep seed={seed} nd={nd} rank={rank} n={len(numels)} param={i} col={j} bits={bad:#x}")
+    gl = None if groups is None else [int(x) for x in groups]
+    A = Z.ShardStep(numels, nd, rank, cap, dtype, groups=gl)
+    F = Z.ShardStep(numels, nd, rank, cap, dtype, groups=gl)
+    live = (rng.random(len(numels)) > 0.2).astype(np.uint8)
+    live[i] = 1
+    p32 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    arena = finite_bits(rng, nd * S, dtype)
+    steps = rng.integers(0, 3, size=len(numels)).astype(np.int32)
+    for X in (A, F):
+        X.p32.copy_(torch.from_numpy(p32))
+        X.m.copy_(torch.from_numpy(p32 * 0.5))
+        X.v.copy_(torch.from_numpy(np.abs(p32)))
+        X.steps.copy_(torch.from_numpy(steps))
+        X.arena.copy_(to_dev16(arena))
+        X.live.copy_(torch.from_numpy(live))
+    before = [t.clone() for t in (A.p32, A.m, A.v, A.steps, A.arena)]
+    grads = [finite_bits(rng, x, dtype) if l else None for x, l in zip(numels, live)]
+    grads[i][rank * s_i + j] = bad
+    _buf, views = placed_views(grads, rng, misalign=bool(rng.random() < 0.5))
+    ptrs = Z.ptr_table(views)
+    A.pack(ptrs)
+    F.flag.zero_()
+    F.pack(ptrs, check=True)
+    got = to_np16(A.packed)
+    rows, want_check = [], 0
+    for b in range(pl.n_buckets):
+        L = int(pl.buckets[b, oracle.B_STRIDE])
+        r_rows = finite_bits(rng, nd * L, dtype).reshape(nd, L)
+        r_rows[rank] = oracle_block(pl, got, b)[rank]
+        rows.append(r_rows)
+        want_check |= oracle.input_check(pl, b, grads, dtype)
+    rdev = [to_dev16(r.reshape(-1)) if r.size else torch.zeros(8, dtype=torch.int16, device=DEV) for r in rows]
+
+    def rows_of(b):
+        return rdev[b], int(pl.buckets[b, oracle.B_STRIDE])
+
+    A.flag.zero_()
+    A.reduce(rows_of)
+    g32 = np.zeros(S, np.float32)
+    for b in range(pl.n_buckets):
+        oracle.reduce_bucket(pl, b, rows[b], dtype, live, g32)
+    torch.cuda.synchronize()
+    assert want_check == 1 and int(F.flag.item()) == 1
+    assert oracle.overflow(pl, g32, live) == 1 and int(A.flag.item()) == 1
+    assert_same_f32(to_np32(A.g32), g32, "g32")
+    hp = (1e-3, 0.9, 0.999, 1e-8, 1.0 / nd)
+    A.adam(*hp)
+    F.reduce_adam(rows_of, *hp)
+    torch.cuda.synchronize()
+    for X in (A, F):
+        for t, t0 in zip((X.p32, X.m, X.v, X.steps, X.arena), before):
+            assert torch.equal(t, t0)
