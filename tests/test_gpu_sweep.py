@@ -229,3 +229,90 @@ def test_random_plan_overflow_skips(seed):
     for X in (A, F):
         for t, t0 in zip((X.p32, X.m, X.v, X.steps, X.arena), before):
             assert torch.equal(t, t0)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_zero3_schedule(seed):
+    """Random layered models (1 to 12 layers of 1 to 6 parameters, empty ones included) through
+    ZeRO-3's schedule, one stream or prefetch: every gather (forward and backward) against the
+    oracle's unpack, the gather order, each layer's packed gradients, the reduced shard and flag,
+    then Adam, against the oracle."""
+    rng = np.random.default_rng(20_000 + seed)
+    nd = int(rng.choice(NDS))
+    rank = int(rng.integers(0, nd))
+    n_layers = int(rng.integers(1, 13))
+    numels, groups = [], []
+    for layer in range(n_layers):
+        for _ in range(int(rng.integers(1, 7))):
+            k = rng.random()
+            numels.append(0 if k < 0.1 else int(rng.integers(1, 2 * nd + 2)) if k < 0.4 else
+                          int(rng.integers(1, 30000)))
+            groups.append(layer)
+    dtype = BF16 if rng.random() < 0.5 else FP16
+    prefetch = bool(rng.random() < 0.5)
+    say(f"zero3 sweep seed={seed} nd={nd} rank={rank} layers={n_layers} n={len(numels)} prefetch={prefetch}")
+    st = Z.ShardStep(numels, nd, rank, 0, dtype, groups=groups)
+    pl = oracle.plan(numels, nd, rank, 0, np.array(groups, np.int32))
+    assert pl.n_buckets == n_layers
+    S = pl.shard_len
+    lp = [finite_bits(rng, x, dtype) for x in numels]
+    arena = np.zeros(nd * S, np.uint16)
+    for b in range(pl.n_buckets):
+        oracle_block(pl, arena, b)[:] = oracle.pack_bucket(pl, b, lp)
+    st.arena.copy_(to_dev16(arena))
+    p32 = (rng.standard_normal(S) * 0.02).astype(np.float32)
+    st.p32.copy_(torch.from_numpy(p32))
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    steps = np.zeros(len(numels), np.int32)
+    live = (rng.random(len(numels)) > 0.2).astype(np.uint8)
+    st.live.copy_(torch.from_numpy(live))
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch)
+
+    def check_gather(lid, params):
+        outs = [np.zeros(x, np.uint16) for x in numels]
+        oracle.unpack_bucket(pl, lid, oracle_block(pl, arena, lid).copy(), outs)
+        for i, view in zip(z3.layers[lid], params):
+            got = to_np16(view)
+            assert np.array_equal(got, outs[i]) and np.array_equal(got, lp[i]), (lid, i)
+
+    grads = [finite_bits(rng, x, dtype) if l else None for x, l in zip(numels, live)]
+    gptrs = Z.ptr_table([None if g is None else to_dev16(g) for g in grads])
+    rows = [finite_bits(rng, nd * int(pl.buckets[b, oracle.B_STRIDE]), dtype).reshape(nd, -1)
+            for b in range(pl.n_buckets)]
+    want_packed = []
+    for b in range(pl.n_buckets):
+        want = np.full((nd, pl.buckets[b, oracle.B_STRIDE]), SENT16, dtype=np.uint16)
+        oracle.pack_bucket(pl, b, grads, out=want)
+        want_packed.append(want)
+        rows[b][rank] = want[rank]
+    rdev = [to_dev16(r.reshape(-1)) if r.size else torch.zeros(8, dtype=torch.int16, device=DEV) for r in rows]
+    out = torch.full_like(st.packed, SENT16)
+    st.flag.zero_()
+    st.g32.fill_(-3.0)
+    z3.forward(check_gather)
+    z3.backward(lambda lid: gptrs, lambda lid: (rdev[lid], int(pl.buckets[lid, oracle.B_STRIDE])), check_gather,
+                out=out)
+    assert z3.order == list(range(n_layers)) + list(range(n_layers - 2, -1, -1))
+    torch.cuda.synchronize()
+    got_out = to_np16(out)
+    for b in range(pl.n_buckets):
+        assert np.array_equal(oracle_block(pl, got_out, b), want_packed[b]), f"packed layer {b}"
+    g32 = np.full(S, -3.0, np.float32)
+    for b in range(pl.n_buckets):
+        oracle.reduce_bucket(pl, b, rows[b], dtype, live, g32)
+    assert_same_f32(to_np32(st.g32), g32, "g32")
+    assert int(st.flag.item()) == oracle.overflow(pl, g32, live) == 0
+    hp = oracle.AdamHP(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, grad_scale=1.0 / nd)
+    st.adam(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.grad_scale)
+    oracle.adam(pl, g32, p32, m, v, live, steps, hp, 0, arena, dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np32(st.steps), steps)
+    assert_close_f32(to_np32(st.p32), p32, "p32")
+    assert_close_f32(to_np32(st.m), m, "m")
+    assert_close_f32(to_np32(st.v), v, "v", abs_=8 * 2.0 ** -149, rel=2e-6)
+    ever = np.zeros(S, dtype=bool)
+    for i in np.flatnonzero(live):
+        o, s_ = pl.params[i, oracle.P_OFFSET], pl.params[i, oracle.P_SHARD]
+        ever[o:o + s_] = True
+    check_arena(pl, to_np16(st.arena), arena, to_np32(st.p32), p32, ever, dtype, "arena")
