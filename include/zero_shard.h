@@ -306,9 +306,11 @@ zero_status zero_shard_init(const zero_plan* plan, const void* const* d_src_ptrs
 
 /* zero_pack_bucket, and OR 1 into *d_flag when a gradient element that the call reads is
  * inf or NaN or has |x| > 2^126 / Nd.  Below that bound no fp32 sum of Nd such values can
- * overflow (each term is below 2^126 / Nd, so every partial sum stays below 2^126), so a flag
- * that is clear on every rank means every reduced sum is finite.  A finite value above the
- * bound flags the step although the sums might not overflow: a conservative skip, which
+ * overflow: with rounding, a partial sum of k terms stays below k * (2^126 / Nd) *
+ * (1 + 2^-24)^k < 2^126 * 1.004 < 2^128 for every Nd a plan allows (Nd <= 65535), so a flag
+ * that is clear on every rank means every reduced sum is finite.  The comparison is exact:
+ * the threshold is the largest 16-bit magnitude whose value times Nd is at most 2^126.  A
+ * finite value above the bound flags the step although the sums might not overflow: a conservative skip, which
  * needs |g| near 2^126 / Nd (never reached by fp16; for bf16 a scaled gradient already
  * beyond any usable loss scale).  Never clears the flag.
  *   d_flag   device int32

@@ -249,3 +249,4 @@ def test_empty_buckets_and_shards_take_null_buffers():
     E.unpack(empty)
     torch.cuda.synchronize()
     assert torch.all(E.steps == 2) and int(E.flag.item()) == 0
+

@@ -15,6 +15,9 @@
 // and a funnel shift (load8_realigned); chunks that straddle parameters, padding or a row gap
 // fall back to per-element work.  The unpack is driven by its output too, in per-parameter
 // chunk space.
+#include <cmath>
+#include <cstring>
+
 #include "zs_common.h"
 
 namespace zs {
@@ -33,25 +36,25 @@ constexpr int kPackRows = ZS_PACK_ROWS;          // rows per block iteration of 
 constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
 
 // The input check of the checked pack: true if one of the eight 16-bit values is inf or NaN
-// or larger in magnitude than `limit` (2^126 / Nd: below it no fp32 sum of Nd values overflows).
-template <int DT>
-__device__ __forceinline__ bool out_of_range8(const uint4& v, float limit) {
+// or larger in magnitude than 2^126 / Nd (below it no fp32 sum of Nd values overflows).  For
+// bf16 and fp16 alike, finite magnitudes order as their bit patterns with the sign cleared, and
+// every inf or NaN pattern lies above every finite one, so the test is one unsigned compare
+// per value against `limit`: the largest magnitude pattern whose value v has v * Nd <= 2^126
+// exactly (check_limit_bits on the host).
+__device__ __forceinline__ bool out_of_range8(const uint4& v, uint32_t limit) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     bool bad = false;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const float lo = to_f32<DT>(w[t] & 0xffffu), hi = to_f32<DT>(w[t] >> 16);
-        bad |= !(fabsf(lo) <= limit) || !(fabsf(hi) <= limit);
-    }
+    for (int t = 0; t < 4; ++t) bad |= ((w[t] & 0x7fffu) > limit) | (((w[t] >> 16) & 0x7fffu) > limit);
     return bad;
 }
 
 // Generic per-thread pack of one 8-column chunk of row k (parameter boundaries, padding,
 // row gaps, dead parameters, unaligned sources).  i is the first parameter with end > x.
-template <int DT, bool CHECK>
+template <bool CHECK>
 __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, int64_t k, int64_t x,
                                                    const uint16_t* const* __restrict__ grads, uint16_t* dst,
-                                                   float limit, bool& bad) {
+                                                   uint32_t limit, bool& bad) {
     if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) {
         const uint16_t* g = grads[i];
         if (!g) return;  // no gradient this step: leave the slots alone
@@ -67,7 +70,7 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
             for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
             v = pack8(h);
         }
-        if constexpr (CHECK) bad |= out_of_range8<DT>(v, limit);
+        if constexpr (CHECK) bad |= out_of_range8(v, limit);
         store16(dst, v);
         return;
     }
@@ -86,7 +89,7 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
         }
         keep |= 1u << t;
     }
-    if constexpr (CHECK) bad |= out_of_range8<DT>(pack8(h), limit);
+    if constexpr (CHECK) bad |= out_of_range8(pack8(h), limit);
     if (keep == 0xffu) {
         store16(dst, pack8(h));
     } else {
@@ -120,9 +123,9 @@ __device__ __forceinline__ int staged_search(const PackMeta* sm, int cnt, int64_
     return lo;
 }
 
-template <int DT, bool CHECK>
+template <bool CHECK>
 __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, int t0, int64_t k, int64_t x,
-                                                  uint16_t* dst, float limit, bool& bad) {
+                                                  uint16_t* dst, uint32_t limit, bool& bad) {
     if (t0 < cnt && sm[t0].off <= x && x + kChunk <= sm[t0].end) {
         const PackMeta& m = sm[t0];
         if (!m.g) return;  // no gradient this step
@@ -137,7 +140,7 @@ __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, i
             for (int t = 0; t < 8; ++t) h[t] = (e0 + t < m.numel) ? gg[e0 + t] : uint16_t(0);
             v = pack8(h);
         }
-        if constexpr (CHECK) bad |= out_of_range8<DT>(v, limit);
+        if constexpr (CHECK) bad |= out_of_range8(v, limit);
         store16(dst, v);
         return;
     }
@@ -157,7 +160,7 @@ __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, i
         }
         keep |= 1u << t;
     }
-    if constexpr (CHECK) bad |= out_of_range8<DT>(pack8(h), limit);
+    if constexpr (CHECK) bad |= out_of_range8(pack8(h), limit);
     if (keep == 0xffu) {
         store16(dst, pack8(h));
     } else {
@@ -173,11 +176,11 @@ __device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, i
 // parameter with a 16-byte aligned gradient (decided once per block from scalar loads), each
 // thread issues the loads of its rows before any store.
 // CHECK: also OR 1 into *flag when a gradient element is non-finite or above `limit`.
-template <int DT, bool CHECK>
+template <bool CHECK>
 __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t tile0,
                                                       int64_t n_tile, int64_t n_rg,
                                                       const uint16_t* const* __restrict__ grads,
-                                                      uint16_t* __restrict__ packed, float limit,
+                                                      uint16_t* __restrict__ packed, uint32_t limit,
                                                       int32_t* __restrict__ flag) {
     __shared__ PackMeta sm[kStageMax];
     const int64_t n_work = n_tile * n_rg;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
                     for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
                     v[u] = pack8(h);
                 }
-                if constexpr (CHECK) bad |= out_of_range8<DT>(v[u], limit);
+                if constexpr (CHECK) bad |= out_of_range8(v[u], limit);
             }
 #pragma unroll
             for (int u = 0; u < kPackRows; ++u) {
@@ -243,13 +246,13 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base,
             if (x < b_base || x >= b_base + b_stride) continue;
             const int t0 = staged_search(sm, int(cnt), x);
             for (int64_t k = k0; k < kend; ++k)
-                pack_chunk_staged<DT, CHECK>(sm, int(cnt), t0, k, x, packed + k * b_stride + (x - b_base), limit, bad);
+                pack_chunk_staged<CHECK>(sm, int(cnt), t0, k, x, packed + k * b_stride + (x - b_base), limit, bad);
             continue;
         }
         if (x < b_base || x >= b_base + b_stride) continue;
         const int64_t i = param_of_column(P, x);
         for (int64_t k = k0; k < kend; ++k)
-            pack_chunk_generic<DT, CHECK>(P, i, k, x, grads, packed + k * b_stride + (x - b_base), limit, bad);
+            pack_chunk_generic<CHECK>(P, i, k, x, grads, packed + k * b_stride + (x - b_base), limit, bad);
     }
     if constexpr (CHECK) flag_wave(bad, flag);
 }
@@ -410,6 +413,32 @@ using namespace zs;
 
 static const int64_t* bucket_row(const zero_plan* plan, int64_t b) { return plan->h_bucket + b * kBucketFields; }
 
+// Value of a 16-bit pattern with the sign cleared (exact in double).
+static double half_bits_value(int dtype, uint32_t b) {
+    if (dtype == ZERO_BF16) {
+        const uint32_t w = b << 16;
+        float f;
+        std::memcpy(&f, &w, sizeof f);
+        return double(f);
+    }
+    const int e = int((b >> 10) & 31u), m = int(b & 1023u);
+    return e == 0 ? std::ldexp(double(m), -24) : std::ldexp(double(1024 + m), e - 25);
+}
+
+// The checked pack's threshold: the largest finite magnitude pattern b with value(b) * nd <=
+// 2^126, the product exact in double (at most 11 significant bits times nd < 2^31).  Values
+// grow with b, so a binary search finds it; for fp16 it is the largest finite pattern.
+static uint32_t check_limit_bits(int dtype, int64_t nd) {
+    const double bound = std::ldexp(1.0, 126);
+    uint32_t lo = 0, hi = dtype == ZERO_BF16 ? 0x7f7fu : 0x7bffu;  // largest finite magnitudes
+    if (half_bits_value(dtype, hi) * double(nd) <= bound) return hi;
+    while (lo + 1 < hi) {  // value(lo) * nd <= bound < value(hi) * nd
+        const uint32_t mid = (lo + hi) / 2;
+        if (half_bits_value(dtype, mid) * double(nd) <= bound) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 static zero_status pack_common(const zero_plan* plan, int64_t b, const void* const* d_grad_ptrs, void* d_packed,
                                int32_t* d_flag, bool check, void* stream, const char* who) {
     zero_status st = check_device(plan);
@@ -427,16 +456,13 @@ static zero_status pack_common(const zero_plan* plan, int64_t b, const void* con
     hipStream_t s = (hipStream_t)stream;
     const uint16_t* const* grads = reinterpret_cast<const uint16_t* const*>(d_grad_ptrs);
     uint16_t* packed = static_cast<uint16_t*>(d_packed);
-    const float limit = ldexpf(1.0f, 126) / float(plan->nd);
+    const uint32_t limit = check ? check_limit_bits(plan->dtype, plan->nd) : 0u;
     if (!check)
-        pack_kernel<0, false><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed, limit,
-                                                   nullptr);
-    else if (plan->dtype == ZERO_BF16)
-        pack_kernel<ZERO_BF16, true><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed,
-                                                          limit, d_flag);
+        pack_kernel<false><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed, limit,
+                                                nullptr);
     else
-        pack_kernel<ZERO_FP16, true><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed,
-                                                          limit, d_flag);
+        pack_kernel<true><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed, limit,
+                                               d_flag);
     return check_launch(who);
 }
 
