@@ -52,6 +52,13 @@
  *   zero_last_error() returns a thread-local message for the last failing call.
  *   A plan stays valid after any failed hot call.
  *
+ * Aliasing:
+ *   The buffers a call writes must not overlap one another or any buffer the same call reads,
+ *   except the arrays a call updates in place (p32, m, v, step counts, the flag, the loss
+ *   scaler): the kernels are compiled on the assumption that distinct pointers do not alias.
+ *   The per-parameter flats one zero_unpack writes must not overlap each other (tables that
+ *   are only read, such as the gradients of a pack, may name overlapping or shared buffers).
+ *
  * Empty work:
  *   A call with nothing to move -- a per-bucket call on a bucket whose rows are empty
  *   (L_b = 0: only parameters of numel 0), or a shard-wide call on a plan whose shard has no
