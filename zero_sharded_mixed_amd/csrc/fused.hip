@@ -18,10 +18,6 @@
 
 namespace zs {
 
-#ifndef ZS_FUSED_PREFETCH
-#define ZS_FUSED_PREFETCH 1
-#endif
-
 template <int DT>
 __global__ __launch_bounds__(kBlock) void reduce_adam_kernel(DevPlan P, int64_t b_base, int64_t b_row,
                                                              int64_t b_stride, int64_t tile0, int64_t n_tile,
@@ -55,23 +51,16 @@ __global__ __launch_bounds__(kBlock) void reduce_adam_kernel(DevPlan P, int64_t 
         const bool one_param = whole || (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]);
         const bool vec = mask == 0xffu && one_param;
         float4 p0, p1, m0, m1, v0, v1;
-#if ZS_FUSED_PREFETCH
         if (vec) {  // the state loads go out with the rows' loads, not after the sum
             p0 = load4f(p32 + x), p1 = load4f(p32 + x + 4);
             m0 = load4f(m + x), m1 = load4f(m + x + 4);
             v0 = load4f(v + x), v1 = load4f(v + x + 4);
         }
-#endif
         float acc[8];
         reduce_rows8<DT>(rows + c, P.nd, row_stride, acc);
         if (vec) {
             // eight columns of one live parameter: the vector update
             const float2 sc = whole ? sc_u : scal[i];
-#if !ZS_FUSED_PREFETCH
-            p0 = load4f(p32 + x), p1 = load4f(p32 + x + 4);
-            m0 = load4f(m + x), m1 = load4f(m + x + 4);
-            v0 = load4f(v + x), v1 = load4f(v + x + 4);
-#endif
             float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
             float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
             float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};

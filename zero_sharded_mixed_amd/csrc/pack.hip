@@ -26,9 +26,6 @@ namespace zs {
 #ifndef ZS_PACK_ROWS
 #define ZS_PACK_ROWS 2
 #endif
-#ifndef ZS_UNPACK_UNIFORM_K
-#define ZS_UNPACK_UNIFORM_K 1
-#endif
 #ifndef ZS_UNPACK_UNROLL
 #define ZS_UNPACK_UNROLL 2
 #endif
@@ -327,7 +324,6 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_bas
         const bool whole = ua >= u0 && ub <= u1 && iu < P.n && ucb <= ua && ucend >= ub;
         if (whole) {
             if (!out) continue;  // every chunk of the group belongs to a skipped parameter
-#if ZS_UNPACK_UNIFORM_K
             // Rows at least as long as the group: find the group's first row once per block;
             // each thread's chunk is then in that row or the next.
             constexpr int64_t kSpanElems = kUnpackUnroll * kUTileChunks * kChunk;
@@ -350,7 +346,6 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_bas
                 }
                 continue;
             }
-#endif
 #pragma unroll
             for (int t = 0; t < kUnpackUnroll; ++t)
                 unpack_chunk(ua + t * kUTileChunks + threadIdx.x, ucb, numel, s, col, inv_s, b_stride, gathered, out);
