@@ -10,7 +10,11 @@ buckets, bf16 gradients and parameters, fp32 master / momentum / variance, with 
 virtual ranks' gradients packed beforehand (their rows are what a reduce-scatter would
 deliver).  Inputs are resident in HBM before timing starts.
 
-Prints one JSON line (rank 0).  value = algorithmic HBM bytes of the step / step time.
+Prints one JSON line (rank 0).  value = algorithmic HBM bytes of the step / step time.  The
+line also carries per-stage times and roofline fractions, the fused path (`fused`: checked
+pack, reduce + Adam in one kernel per bucket), the step replayed as a HIP graph (`graph`),
+ZeRO-3's step with one bucket per layer (`zero3`, one stream and `prefetch`), torch's device
+copy as a reference, and the CPU oracle's throughput (`cpu_baseline`).
 """
 from __future__ import annotations
 
