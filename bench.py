@@ -428,6 +428,18 @@ def copy_reference(device, nbytes=2 << 30, reps=10):
 
 # --------------------------------------------------------------------------- CPU side --
 
+def host_cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, max_elems: int):
     """The oracle, single-threaded, on a prefix of the same parameter list (the whole step:
     pack, reduce, overflow, Adam, unpack), inputs drawn from the same distributions."""
@@ -478,6 +490,7 @@ def cpu_baseline(w, max_elems: int):
     total = ab["pack"] + ab["reduce"] + ab["adam"] + ab["unpack"]
     names = [n for n, _ in w.params[:keep]]
     return {"value": round(total / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": host_cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "seconds": round(secs, 2), "elem_per_s": round(ab["shard_live"] / secs, 1),
             "sample": f"first {keep} of {len(numels)} parameters ({names[0]} .. {names[-1]}), "
                       f"{int(sub.sum())} elements, one full step (pack, reduce, overflow, Adam, unpack), "
