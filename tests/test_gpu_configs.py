@@ -8,7 +8,6 @@ positions (with every parameter's first and last slice column, row boundaries an
 positions among them).  The oracle's inputs always come from the seeded generators, never from
 a GPU output: a sampled column's rows are gathered from the source gradients, and the oracle
 carries the sampled columns' Adam state from step to step itself."""
-import math
 
 import numpy as np
 import pytest

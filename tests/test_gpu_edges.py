@@ -11,7 +11,7 @@ import torch
 import oracle
 import zero_sharded_mixed_amd as Z
 from zero_sharded_mixed_amd import _binding as B
-from gpu_harness import (DEV, assert_close_f32, assert_same_f32, ragged_numels, random_bits, say, to_dev16, to_np16,
+from gpu_harness import (DEV, assert_close_f32, assert_same_f32, ragged_numels, random_bits, to_dev16, to_np16,
                          to_np32)
 
 pytestmark = pytest.mark.gpu
