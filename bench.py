@@ -518,7 +518,8 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
     """Reduce rocprofv3 CSV output (root/trace: --kernel-trace --stats; root/FETCH_SIZE and
     root/WRITE_SIZE: one --pmc pass each) to a short text summary, and record the HBM bytes
     per launch of every pipeline kernel in profiles/traffic.json.  The counters are scaled by
-    what they read for torch's 2 GiB device copy (2 GiB fetched, 2 GiB written)."""
+    what they read for torch's 2 GiB device copy (2 GiB fetched, 2 GiB written).  Without
+    root/FETCH_SIZE the summary holds the kernel times only and traffic.json is left alone."""
     import csv
     import glob
 
@@ -540,6 +541,8 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
+    if not glob.glob(os.path.join(root, "FETCH_SIZE")):  # a kernel trace alone: no traffic section
+        return "\n".join(lines) + "\n"
     traffic = {}
     counters = {}
     for cname in ("FETCH_SIZE", "WRITE_SIZE"):

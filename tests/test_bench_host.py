@@ -70,3 +70,18 @@ def test_more_than_one_gpu_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_summarize_trace_only(tmp_path, monkeypatch):
+    """A directory with only a kernel trace gives the kernel-time table and leaves the traffic
+    record untouched."""
+    root = tmp_path / "prof"
+    _write_csv(str(root / "trace" / "x" / "k_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+               [["void zs::adam_kernel<1, 8>(zs::DevPlan, zs::AdamArgs, long)", 3, 3_000_000, 1_000_000, 100.0,
+                 990_000, 1_010_000]])
+    out = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    text = bench.summarize_profiles(str(root), "toy", "rocprofv3 --kernel-trace --stats -- python3 bench.py")
+    assert "| adam | 3 | 1000.0 |" in text and "HBM traffic" not in text
+    assert not out.exists()
