@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Shard-step throughput of the ZeRO-1/2 per-rank pipeline on one MI355X.
 
-One step = every hot-path stage for one rank over one batch of synthetic gradients:
-pack this rank's gradient buckets rank-major, reduce the Nd virtual ranks' rows into the fp32
-shard (overflow flag fused), the fused mixed-precision Adam step writing the 16-bit all-gather
-row, and the unpack of the gathered buckets into the per-parameter flats.  The default
-workload is a GPT-2 1.5B-shaped parameter list at Nd = 8 virtual ranks, rank 0, 500M-element
-buckets, bf16 gradients and parameters, fp32 master / momentum / variance, with the other
-virtual ranks' gradients packed beforehand (their rows are what a reduce-scatter would
-deliver).  Inputs are resident in HBM before timing starts.
+One step = every hot-path stage for one rank over one batch of synthetic gradients: pack this
+rank's gradient buckets rank-major, reduce the Nd virtual ranks' rows into the fp32 shard
+(overflow flag fused), the fused mixed-precision Adam step writing the 16-bit all-gather row,
+and the unpack of the gathered buckets into the per-parameter flats.  Inputs are resident in
+HBM before timing starts; the boundary takes device buffers, so no PCIe transfer is involved.
 
-Prints one JSON line (rank 0).  value = algorithmic HBM bytes of the step / step time.  The
-line also carries per-stage times and roofline fractions, the fused path (`fused`: checked
-pack, reduce + Adam in one kernel per bucket), the step replayed as a HIP graph (`graph`),
-ZeRO-3's step with one bucket per layer (`zero3`, one stream and `prefetch`), torch's device
-copy as a reference, and the CPU oracle's throughput (`cpu_baseline`).
+The reported line is the largest list: the 7.5B paper-style list (72 layers, d = 2880,
+odd-sized biases forcing padding) at Nd = 64 virtual ranks, rank 63, fp16 gradients with a
+2^16 loss scale, 500M-element buckets.  The other lists (GPT-2 1.5B at Nd = 8 with the ZeRO-3
+leg, Llama-7B at Nd = 8, the ragged 10,000-parameter list at Nd = 1024) run in child processes
+of this one and are carried as sub-objects under `workloads`.
+
+Prints one JSON line.  value = algorithmic HBM bytes of the step / step time (GB/s).  The line
+also carries the per-stage times and roofline fractions (`kernels`), the dominant stage's
+`roofline` (with the HBM bytes per launch that rocprofv3 counters measured on the current
+kernel sources, or null), the fused path (`fused`: checked pack, reduce + Adam in one kernel
+per bucket), the step replayed as a HIP graph (`graph`), the achievable bandwidth of the
+kernels' access patterns on this device (`ceilings`, hand-written probes timed in this run),
+and the CPU oracle timed on the host (`cpu_baseline`: all cores and one thread).
 """
 from __future__ import annotations
 
@@ -22,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -35,6 +41,8 @@ import zero_sharded_mixed_amd as Z  # noqa: E402  (fails at first call if the HI
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "shard step GB/s & elem/s (pack+reduce+Adam) vs HBM peak, 1 MI355X"
+HEADLINE = 4
+OTHERS = (2, 3, 5)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOAD_IDS = {1: "mlp-nd8-r3", 2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63",
                 5: "ragged-10k-nd1024-r517"}
@@ -46,10 +54,11 @@ WORKLOAD_TEXT = {
        "betas (0.9, 0.999), eps 1e-8",
     3: "Llama-7B-shaped parameter list (32 layers, d=4096, ffn 11008, vocab 32000, untied head); Nd=8, rank 5, "
        "500M-element buckets; bf16 grads N(0,1e-3) with 1% exact zeros; fp32 master / m / v",
-    4: "7.5B paper-style list (72 layers, d=2880, odd-sized biases forcing padding); Nd=64, rank 63; fp16 grads "
-       "N(0,1e-3) x 2^16 loss scale; fp32 master / m / v",
-    5: "ragged list of 10,000 parameters, numel log-uniform in [1, 4M]; Nd=1024, rank 517; 30% without gradient; "
-       "fp16 grads N(0,1e-2); fp32 master / m / v",
+    4: "7.5B paper-style parameter list (72 layers, d=2880, vocab 50257, untied head, odd-sized biases forcing "
+       "padding; 869 params, Psi 7.46e9); Nd=64 virtual ranks, rank 63, 500M-element buckets; fp16 grads "
+       "N(0,1e-3) x 2^16 loss scale; fp32 master N(0,0.02) / m / v; Adam lr 1e-3, betas (0.9, 0.999), eps 1e-8",
+    5: "ragged list of 10,000 parameters, numel log-uniform in [1, 4M]; Nd=1024, rank 517, 500M-element buckets; "
+       "30% without gradient; fp16 grads N(0,1e-2); fp32 master / m / v",
 }
 
 
@@ -111,72 +120,79 @@ def measured_traffic(kernel: str, workload: str):
 
 # --------------------------------------------------------------------------- GPU side --
 
-def setup_gpu(w, device):
+class Ctx:
+    """One rank's buffers and inputs for a workload, resident on the device."""
+
+    def __init__(self, st, own_ptrs, own_out, rows_of, lp, lp_ptrs, live):
+        self.st, self.own_ptrs, self.own_out, self.rows_of = st, own_ptrs, own_out, rows_of
+        self.lp, self.lp_ptrs, self.live = lp, lp_ptrs, live
+
+
+def _model(w, device):
+    """Plan, fp32 master shard, the 16-bit model (one flat buffer, per-parameter views) and the
+    all-gather arena holding it (every rank holds the full model before the step)."""
     import workloads as W
 
-    torch.cuda.set_device(device)
-    t0 = time.time()
     st = Z.ShardStep(w.numels, w.nd, w.rank, w.bucket_bytes, w.dtype, device=device)
     s = st.summary
     log(f"[bench] plan: n={s.n_params} nd={s.nd} rank={s.rank} buckets={s.n_buckets} shard={s.shard_numel} "
-        f"psi={s.padded_total} ({time.time() - t0:.1f}s)")
+        f"psi={s.padded_total}")
     masters = W.masters(w, device)
     st.init_master(Z.ptr_table(masters), 0)
-    lp = [m.to(torch.bfloat16 if w.dtype == W.BF16 else torch.float16) for m in masters]
+    lp = W.to_16bit(masters, w.dtype)
     del masters
     lp_ptrs = Z.ptr_table(lp)
-    st.pack(lp_ptrs, out=st.arena)  # every rank holds the full model: the gathered rows start equal
+    st.pack(lp_ptrs, out=st.arena)
+    return st, lp, lp_ptrs
+
+
+def setup_full(w, device):
+    """Full emulation: every virtual rank's whole gradient list is generated and packed; rank
+    r's is re-packed inside each timed step."""
+    import workloads as W
+
+    t0 = time.time()
+    st, lp, lp_ptrs = _model(w, device)
     live = W.live_mask(w, 0)
     st.live.copy_(torch.from_numpy(live))
-    # every virtual rank's packed gradients; rank r's are re-packed inside each timed step
-    packed_all = torch.empty((w.nd, int(s.arena_numel)), dtype=torch.int16, device=device)
-    own = None
+    packed_all = torch.empty((w.nd, int(st.summary.arena_numel)), dtype=torch.int16, device=device)
+    own_ptrs = None
     for k in range(w.nd):
         g = W.grads(w, 0, k, device)
-        gl = [t if l else None for t, l in zip(g, live)]
-        ptrs = Z.ptr_table(gl)
+        ptrs = Z.ptr_table([t if l else None for t, l in zip(g, live)])
         st.pack(ptrs, out=packed_all[k])
         if k == w.rank:
-            own = (gl, ptrs)
-        else:
-            del gl, g
+            own_ptrs = ptrs
+        del g, ptrs
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB ({time.time() - t0:.1f}s)")
     flat = packed_all.view(-1)
-    stride = int(s.arena_numel)
+    stride = int(st.summary.arena_numel)
 
     def rows_of(b):
         bk = st.buckets[b]
         return flat[bk.block_offset + w.rank * bk.row_stride:], stride
 
-    return st, own, packed_all, rows_of, lp, lp_ptrs, live
+    ctx = Ctx(st, own_ptrs, packed_all[w.rank], rows_of, lp, lp_ptrs, live)
+    ctx.packed_all = packed_all
+    return ctx
 
 
-def setup_gpu_rows(w, device):
+def setup_rows(w, device):
     """Row-only emulation (lists whose Nd full gradient copies would not fit): the other
-    virtual ranks' rows r are generated directly per bucket, with the positions a packer leaves
-    zero (padding, dead parameters, the row gap) set to +0.  Row r is this rank's own packed
-    row, copied once: the gradients are the same in every timed step, so the reduce reads
-    exactly what the step's pack writes."""
+    virtual ranks' rows r are generated directly, one block per bucket, with the positions a
+    packer leaves zero (padding, dead parameters, the row gap) set to +0.  Row r is this rank's
+    own packed row, copied once: the gradients are the same in every timed step, so the reduce
+    reads exactly what the step's pack writes."""
     import workloads as W
 
-    torch.cuda.set_device(device)
     t0 = time.time()
-    st = Z.ShardStep(w.numels, w.nd, w.rank, w.bucket_bytes, w.dtype, device=device)
-    s = st.summary
-    log(f"[bench] plan: n={s.n_params} nd={s.nd} rank={s.rank} buckets={s.n_buckets} shard={s.shard_numel} "
-        f"psi={s.padded_total} ({time.time() - t0:.1f}s)")
-    masters = W.masters(w, device)
-    st.init_master(Z.ptr_table(masters), 0)
-    lp = [m.to(torch.bfloat16 if w.dtype == W.BF16 else torch.float16) for m in masters]
-    del masters
-    lp_ptrs = Z.ptr_table(lp)
-    st.pack(lp_ptrs, out=st.arena)
+    st, lp, lp_ptrs = _model(w, device)
     live = W.live_mask(w, 0)
     st.live.copy_(torch.from_numpy(live))
     g = W.grads(w, 0, w.rank, device)
-    gl = [t if l else None for t, l in zip(g, live)]
-    own_ptrs = Z.ptr_table(gl)
+    own_ptrs = Z.ptr_table([t if l else None for t, l in zip(g, live)])
+    del g
     st.pack(own_ptrs)
     info = [Z.zero_plan_param_info(st.plan, i) for i in range(st.n)]
     recv = []
@@ -189,13 +205,9 @@ def setup_gpu_rows(w, device):
                 real = max(0, min(p.shard_size, p.numel - w.rank * p.shard_size))
                 keep[p.bucket_col:p.bucket_col + real] = True
         zero = torch.from_numpy(~keep).to(device)
-        blk = torch.empty((w.nd, L), dtype=torch.int16, device=device)
-        for k in range(w.nd):
-            if k == w.rank:
-                blk[k].copy_(st.own_row(st.packed, b))
-            else:
-                blk[k].copy_(W.remote_row(w, 0, k, b, L, device).view(torch.int16))
-                blk[k].masked_fill_(zero, 0)
+        blk = W.remote_rows(w, 0, b, L, device).view(torch.int16)
+        blk.masked_fill_(zero.unsqueeze(0), 0)
+        blk[w.rank].copy_(st.own_row(st.packed, b))
         recv.append(blk)
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 2**30:.1f} GiB ({time.time() - t0:.1f}s)")
@@ -203,26 +215,23 @@ def setup_gpu_rows(w, device):
     def rows_of(b):
         return recv[b].view(-1), int(st.buckets[b].row_stride)
 
-    return st, (gl, own_ptrs), st.packed, rows_of, lp, lp_ptrs, live
+    return Ctx(st, own_ptrs, st.packed, rows_of, lp, lp_ptrs, live)
 
 
 def setup(w, device):
-    if w.emulation == "full":
-        st, own, packed_all, rows_of, lp, lp_ptrs, live = setup_gpu(w, device)
-        own_out = packed_all[w.rank]
-    else:
-        st, own, own_out, rows_of, lp, lp_ptrs, live = setup_gpu_rows(w, device)
-    return st, own[1], own_out, rows_of, lp, lp_ptrs, live
+    torch.cuda.set_device(device)
+    return setup_full(w, device) if w.emulation == "full" else setup_rows(w, device)
 
 
 PHASES = {"unfused": ("pack", "reduce", "adam", "unpack"), "fused": ("pack", "reduce_adam", "unpack")}
 
 
 def run_gpu(w, ctx, path, steps, warmup):
-    """Time `steps` steps of one path.  unfused: pack -> reduce with the fused overflow check
-    -> Adam -> unpack; fused: pack with the input check -> per-parameter step sizes + per-bucket
-    reduce + Adam in one kernel -> unpack."""
-    st, own_ptrs, own_out, rows_of, lp, lp_ptrs, live = ctx
+    """Time `steps` steps of one path, with HIP events on the kernels' stream around every
+    stage.  unfused: pack -> reduce with the fused overflow check -> Adam -> unpack; fused:
+    pack with the input check -> per-parameter step sizes + per-bucket reduce + Adam in one
+    kernel -> unpack."""
+    st = ctx.st
     b1, b2 = w.betas
     phases = PHASES[path]
 
@@ -233,16 +242,16 @@ def run_gpu(w, ctx, path, steps, warmup):
 
         mark(0)
         st.flag.zero_()
-        st.pack(own_ptrs, out=own_out, check=(path == "fused"))
+        st.pack(ctx.own_ptrs, out=ctx.own_out, check=(path == "fused"))
         mark(1)
         if path == "unfused":
-            st.reduce(rows_of, fused_check=True)
+            st.reduce(ctx.rows_of, fused_check=True)
             mark(2)
             st.adam(w.lr, b1, b2, w.eps, w.grad_scale)
         else:
-            st.reduce_adam(rows_of, w.lr, b1, b2, w.eps, w.grad_scale)
+            st.reduce_adam(ctx.rows_of, w.lr, b1, b2, w.eps, w.grad_scale)
         mark(len(phases) - 1)
-        st.unpack(lp_ptrs)
+        st.unpack(ctx.lp_ptrs)
         mark(len(phases))
 
     for _ in range(warmup):
@@ -273,15 +282,15 @@ def run_graph(w, ctx, steps, warmup):
     calls allocate nothing, never synchronise and clear the flag with a fill kernel, not a
     memset, so the whole step is one graph launch.  Every buffer the captured kernels touch,
     through pointer tables included, stays referenced for the life of the graph."""
-    st, own_ptrs, own_out, rows_of, lp, lp_ptrs, live = ctx
+    st = ctx.st
     b1, b2 = w.betas
 
     def step():
         st.flag.zero_()
-        st.pack(own_ptrs, out=own_out)
-        st.reduce(rows_of, fused_check=True)
+        st.pack(ctx.own_ptrs, out=ctx.own_out)
+        st.reduce(ctx.rows_of, fused_check=True)
         st.adam(w.lr, b1, b2, w.eps, w.grad_scale)
-        st.unpack(lp_ptrs)
+        st.unpack(ctx.lp_ptrs)
 
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -299,32 +308,31 @@ def run_graph(w, ctx, steps, warmup):
     return ms
 
 
-def run_zero3(w, ctx, steps, warmup, device, graph=True):
+def run_zero3(w, ctx, steps, warmup, device, graph=True, prefetch=False):
     """ZeRO-3's step on the same list with one bucket per layer (workloads.layer_groups): the
     forward pass gathers every layer's parameters (unpack into a scratch buffer), the backward
     pass gathers all but the last layer again and reduce-scatters each layer's gradients (pack
     + reduce) right after it, then Adam writes this rank's 16-bit shard.  Full emulation: every
     virtual rank's gradients are packed for the per-layer buckets beforehand; this rank's are
-    re-packed inside each timed step, into the rows the reduce reads.  Timed twice: all on one
-    stream, and with prefetch (the gathers on a second stream into two scratch buffers, the
-    next layer's gather overlapping the current layer's pack and reduce).  With graph=True each
-    step (about 200 launches) is also captured once into a HIP graph and the replays timed."""
+    re-packed inside each timed step, into the rows the reduce reads.  All on one stream; with
+    prefetch=True also with the gathers on a second stream into two scratch buffers.  With
+    graph=True each step (about 200 launches) is also captured into a HIP graph and replayed."""
     import workloads as W
 
-    st2, own_ptrs, _, _, lp, lp_ptrs, live = ctx
+    st2, live = ctx.st, ctx.live
     t0 = time.time()
     z = Z.ShardStep(w.numels, w.nd, w.rank, 0, w.dtype, device=device, groups=W.layer_groups(w))
     z.live.copy_(st2.live)
-    z.init_master(lp_ptrs, w.dtype)  # p32 = row r of the 16-bit model (converted exactly)
-    z.pack(lp_ptrs, out=z.arena)     # every rank holds its row of every layer
+    z.init_master(ctx.lp_ptrs, w.dtype)  # p32 = row r of the 16-bit model (converted exactly)
+    z.pack(ctx.lp_ptrs, out=z.arena)     # every rank holds its row of every layer
     an = int(z.summary.arena_numel)
     packed_all = torch.empty((w.nd, an), dtype=torch.int16, device=device)
     for k in range(w.nd):
         if k == w.rank:
-            z.pack(own_ptrs, out=packed_all[k])
+            z.pack(ctx.own_ptrs, out=packed_all[k])
             continue
-        g = [t if l else None for t, l in zip(W.grads(w, 0, k, device), live)]
-        z.pack(Z.ptr_table(g), out=packed_all[k])
+        g = Z.ptr_table([t if l else None for t, l in zip(W.grads(w, 0, k, device), live)])
+        z.pack(g, out=packed_all[k])
         del g
     flat = packed_all.view(-1)
 
@@ -349,7 +357,7 @@ def run_zero3(w, ctx, steps, warmup, device, graph=True):
             z3.order.clear()
             z3.forward()
             mark(1)
-            z3.backward(lambda lid: own_ptrs, rows_of, out=packed_all[w.rank])
+            z3.backward(lambda lid: ctx.own_ptrs, rows_of, out=packed_all[w.rank])
             mark(2)
             z.adam(w.lr, b1, b2, w.eps, w.grad_scale)
             mark(3)
@@ -398,19 +406,19 @@ def run_zero3(w, ctx, steps, warmup, device, graph=True):
         f"({time.time() - t0:.1f}s)")
     out = measure(z3)
     del z3
-    # the same step with the gathers on a second stream into two scratch buffers
-    z3 = Z.Zero3Schedule(z, prefetch=True)
-    pf = measure(z3)
-    pf["speedup"] = round(out["ms_per_step"] / pf["ms_per_step"], 3)
-    out["prefetch"] = pf
-    del packed_all, z3, z
+    if prefetch:  # the gathers on a second stream into two scratch buffers
+        z3 = Z.Zero3Schedule(z, prefetch=True)
+        pf = measure(z3)
+        pf["speedup"] = round(out["ms_per_step"] / pf["ms_per_step"], 3)
+        out["prefetch"] = pf
+        del z3
+    del packed_all, z
     torch.cuda.empty_cache()
     return out
 
 
 def copy_reference(device, nbytes=2 << 30, reps=10):
-    """GB/s (read + write) of torch's device-to-device copy of a 2 GiB buffer: what a plain
-    streaming kernel reaches on this device, for context next to the 8 TB/s peak."""
+    """GB/s (read + write) of torch's device-to-device copy of a 2 GiB buffer, for context."""
     a = torch.empty(nbytes // 2, dtype=torch.int16, device=device)
     b = torch.empty_like(a)
     b.copy_(a)
@@ -424,6 +432,135 @@ def copy_reference(device, nbytes=2 << 30, reps=10):
     ms = e0.elapsed_time(e1) / reps
     del a, b
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def ceilings(device, adam_cols: int, pack_bytes: int, reps: int = 10):
+    """What plain streams reach on this device, timed here with the hand-written probes of
+    include/zero_probe.h (same launch shape as the pipeline kernels, trivial arithmetic):
+    read-only, write-only and copy over a pack-sized buffer, and Adam's 4-read / 4-write
+    stream mix over an Adam-sized shard (30 B per column).  GB/s of bytes moved; the kernels'
+    fractions of these are reported next to them by the caller."""
+    from zero_sharded_mixed_amd import probe
+
+    def timed(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return {"GBs": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4), "bytes": nbytes,
+                "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    nb = (pack_bytes // 2) // 16 * 16
+    src = torch.empty(nb // 4, dtype=torch.int32, device=device)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=device)
+    probe.write(src)
+    out = {"read": timed(lambda: probe.read(src, sink), nb),
+           "write": timed(lambda: probe.write(dst), nb),
+           "copy": timed(lambda: probe.copy(src, dst), 2 * nb)}
+    del src, dst
+    n = adam_cols // 8 * 8
+    f32 = dict(dtype=torch.float32, device=device)
+    g, p, m, v = (torch.zeros(n, **f32) for _ in range(4))
+    lp = torch.zeros(n, dtype=torch.int16, device=device)
+    out["adam_streams"] = timed(lambda: probe.adam_streams(g, p, m, v, lp), 30 * n)
+    del g, p, m, v, lp
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_workload(w, args, device, headline: bool):
+    """Everything the line reports for one workload: both paths' per-stage times and
+    fractions, the dominant stage's roofline, and the optional graph and ZeRO-3 legs."""
+    import workloads as W
+
+    wid = WORKLOAD_IDS[w.config]
+    ctx = setup(w, device)
+    st = ctx.st
+    shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
+    ab = algorithmic_bytes(w.numels, shard_sizes, ctx.live, w.nd)
+    ne = stage_elements(ab)
+    runs = {}
+    for path in ("unfused", "fused"):
+        ms_p, per_phase, launches, flag = run_gpu(w, ctx, path, args.steps, args.warmup)
+        kernels = {}
+        for p in PHASES[path]:
+            gbs = ab[p] / (per_phase[p] * 1e-3) / 1e9
+            kernels[p] = {"ms": round(per_phase[p], 4), "launches": launches[p], "bytes": ab[p],
+                          "GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                          "elements": ne[p], "elem_per_s": round(ne[p] / (per_phase[p] * 1e-3), 1)}
+        runs[path] = dict(ms=ms_p, kernels=kernels, launches=launches, flag=flag,
+                          bytes=sum(ab[p] for p in PHASES[path]))
+    ms, kernels, launches, flag = (runs["unfused"][k] for k in ("ms", "kernels", "launches", "flag"))
+    step_bytes = runs["unfused"]["bytes"]
+
+    def roofline(kern, name):
+        d = kern[name]
+        per_launch = d["bytes"] // d["launches"]
+        avg_ms = d["ms"] / d["launches"]
+        ach = per_launch / (avg_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": name, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, wid),
+                "bytes_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4)}
+
+    fz = runs["fused"]
+    fused = {"ms_per_step": round(fz["ms"], 4), "speedup": round(ms / fz["ms"], 3),
+             "GBs": round(fz["bytes"] / (fz["ms"] * 1e-3) / 1e9, 1), "step_bytes": fz["bytes"],
+             "elem_per_s": round(ab["shard_live"] / (fz["ms"] * 1e-3), 1), "overflow_flag": fz["flag"],
+             "kernels": fz["kernels"], "roofline": roofline(fz["kernels"], "reduce_adam")}
+    dom = max(kernels, key=lambda p: kernels[p]["ms"])
+    res = {
+        "workload": WORKLOAD_TEXT[w.config], "workload_id": wid, "nd": w.nd, "rank": w.rank, "n_params": w.n,
+        "psi": int(sum(s * w.nd for s in shard_sizes)), "shard_elems": ab["shard_live"],
+        "n_buckets": launches["pack"],
+        "storage": ("bf16" if w.dtype == W.BF16 else "fp16") + " grads/params, fp32 state",
+        "emulation": w.emulation,
+        "ms_per_step": round(ms, 4), "GBs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "elem_per_s": round(ab["shard_live"] / (ms * 1e-3), 1),
+        "grad_elem_per_s": round(ab["numel_live"] / (ms * 1e-3), 1),
+        "step_bytes": step_bytes, "overflow_flag": flag, "kernels": kernels, "fused": fused,
+        "roofline": roofline(kernels, dom),
+    }
+    if not args.no_graph:
+        gms = run_graph(w, ctx, args.steps, args.warmup)
+        res["graph"] = {"ms_per_step": round(gms, 4), "eager_ms_per_step": round(ms, 4),
+                        "speedup": round(ms / gms, 3)}
+    if w.emulation == "full" and not args.no_zero3 and not headline:
+        res["zero3"] = run_zero3(w, ctx, args.steps, args.warmup, device, graph=not args.no_graph,
+                                 prefetch=args.zero3_prefetch)
+    del ctx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_children(configs, args):
+    """Each other workload in a child process of its own (its memory is returned when it
+    exits); returns {workload_id: sub-object} (an `error` entry if a child failed)."""
+    out = {}
+    for c in configs:
+        cmd = [sys.executable, os.path.abspath(__file__), "--child", "--config", str(c), "--steps",
+               str(min(args.steps, args.other_steps)), "--warmup", str(args.warmup)]
+        for flag in ("no_graph", "no_zero3", "zero3_prefetch"):
+            if getattr(args, flag):
+                cmd.append("--" + flag.replace("_", "-"))
+        log(f"[bench] workload {WORKLOAD_IDS[c]} (child process) ...")
+        t0 = time.time()
+        try:
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=args.child_timeout)
+            lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+            out[WORKLOAD_IDS[c]] = json.loads(lines[-1]) if r.returncode == 0 and lines else \
+                {"error": f"exit status {r.returncode}"}
+        except subprocess.TimeoutExpired:
+            out[WORKLOAD_IDS[c]] = {"error": f"timed out after {args.child_timeout} s"}
+        log(f"[bench] workload {WORKLOAD_IDS[c]} done ({time.time() - t0:.1f}s)")
+    return out
 
 
 # --------------------------------------------------------------------------- CPU side --
@@ -440,9 +577,10 @@ def host_cpu_model() -> str:
     return ""
 
 
-def cpu_baseline(w, max_elems: int):
-    """The oracle, single-threaded, on a prefix of the same parameter list (the whole step:
-    pack, reduce, overflow, Adam, unpack), inputs drawn from the same distributions."""
+def cpu_sample(w, max_elems: int, device):
+    """A bounded sample of the workload for the oracle: the longest prefix of the parameter list
+    with at most max_elems elements (at least one parameter), with values drawn from the
+    workload's distributions (on `device`, then copied to the host)."""
     import oracle
     import workloads as W
 
@@ -452,33 +590,45 @@ def cpu_baseline(w, max_elems: int):
         keep += 1
     sub = numels[:keep]
     pl = oracle.plan(sub, w.nd, w.rank, w.bucket_bytes)
-    # values drawn on the device (fast) from the workload's distributions, copied to the host
-    gen = torch.Generator(device="cuda")
+    gen = torch.Generator(device=device)
     gen.manual_seed(W.seed_of(w.config, 0, 0, W.SLOT_GRAD))
     tdt = torch.bfloat16 if w.dtype == W.BF16 else torch.float16
 
-    def bits16(n, std):
-        x = torch.randn(n, generator=gen, device="cuda") * std
+    def bits16(n):
+        x = torch.randn(n, generator=gen, device=device) * (w.grad_std * w.loss_scale)
         return x.to(tdt).view(torch.int16).cpu().numpy().view(np.uint16)
 
-    grads = [bits16(int(x), w.grad_std) for x in sub]
     S = pl.shard_len
-    rows = [bits16(w.nd * int(pl.buckets[b, oracle.B_STRIDE]), w.grad_std).reshape(w.nd, -1)
-            for b in range(pl.n_buckets)]
-    p32 = (torch.randn(S, generator=gen, device="cuda") * w.master_std).cpu().numpy()
+    return {
+        "pl": pl, "sub": sub, "keep": keep,
+        "grads": [bits16(int(x)) for x in sub],
+        "rows": [bits16(w.nd * int(pl.buckets[b, oracle.B_STRIDE])).reshape(w.nd, -1) for b in range(pl.n_buckets)],
+        "p32": (torch.randn(S, generator=gen, device=device) * w.master_std).cpu().numpy(),
+    }
+
+
+def oracle_step(w, smp):
+    """One full step of the oracle over the sample (pack, reduce, overflow, Adam, unpack);
+    returns (seconds, outputs)."""
+    import oracle
+
+    pl = smp["pl"]
+    S = pl.shard_len
+    p32 = smp["p32"].copy()
     m = np.zeros(S, np.float32)
     v = np.zeros(S, np.float32)
     g32 = np.zeros(S, np.float32)
     steps = np.zeros(pl.n, np.int32)
     arena = np.zeros(w.nd * S, np.uint16)
     live = np.ones(pl.n, np.uint8)
-    outs = [np.empty(int(x), np.uint16) for x in sub]
+    outs = [np.empty(int(x), np.uint16) for x in smp["sub"]]
+    packed = [np.zeros((w.nd, int(pl.buckets[b, oracle.B_STRIDE])), np.uint16) for b in range(pl.n_buckets)]
     hp = oracle.AdamHP(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps, grad_scale=w.grad_scale)
     t0 = time.perf_counter()
     for b in range(pl.n_buckets):
-        oracle.pack_bucket(pl, b, grads)
+        oracle.pack_bucket(pl, b, smp["grads"], out=packed[b])
     for b in range(pl.n_buckets):
-        oracle.reduce_bucket(pl, b, rows[b], w.dtype, live, g32)
+        oracle.reduce_bucket(pl, b, smp["rows"][b], w.dtype, live, g32)
     flag = oracle.overflow(pl, g32, live)
     oracle.adam(pl, g32, p32, m, v, live, steps, hp, flag, arena, w.dtype)
     for b in range(pl.n_buckets):
@@ -486,22 +636,50 @@ def cpu_baseline(w, max_elems: int):
         L = int(pl.buckets[b, oracle.B_STRIDE])
         oracle.unpack_bucket(pl, b, arena[base:base + w.nd * L].reshape(w.nd, L), outs)
     secs = time.perf_counter() - t0
-    ab = algorithmic_bytes(sub, pl.params[:, oracle.P_SHARD], live, w.nd)
+    return secs, {"packed": packed, "g32": g32, "p32": p32, "m": m, "v": v, "arena": arena, "outs": outs,
+                  "flag": flag}
+
+
+def cpu_baseline(w, max_elems: int, device="cuda"):
+    """The oracle as it stands, on the host cores of this machine, over a bounded sample of the
+    same workload: once with one thread and once with every CPU this process may run on
+    (sched_getaffinity; the oracle splits each parameter's element loops into disjoint column
+    ranges, so the outputs are identical, which is checked here)."""
+    import oracle
+
+    smp = cpu_sample(w, max_elems, device)
+    pl = smp["pl"]
+    cores = len(os.sched_getaffinity(0))
+    oracle.set_threads(1)
+    t1, ref = oracle_step(w, smp)
+    oracle.set_threads(cores)
+    tn, got = oracle_step(w, smp)
+    oracle.set_threads(1)
+    same = all(np.array_equal(a.view(np.uint8), b.view(np.uint8)) for k in ("g32", "p32", "m", "v", "arena")
+               for a, b in [(ref[k], got[k])])
+    same = same and all(np.array_equal(a, b) for a, b in zip(ref["packed"], got["packed"]))
+    same = same and all(np.array_equal(a, b) for a, b in zip(ref["outs"], got["outs"])) and ref["flag"] == got["flag"]
+    ab = algorithmic_bytes(smp["sub"], pl.params[:, oracle.P_SHARD], np.ones(pl.n, np.uint8), w.nd)
     total = ab["pack"] + ab["reduce"] + ab["adam"] + ab["unpack"]
-    names = [n for n, _ in w.params[:keep]]
-    return {"value": round(total / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "cpu_model": host_cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
-            "seconds": round(secs, 2), "elem_per_s": round(ab["shard_live"] / secs, 1),
-            "sample": f"first {keep} of {len(numels)} parameters ({names[0]} .. {names[-1]}), "
-                      f"{int(sub.sum())} elements, one full step (pack, reduce, overflow, Adam, unpack), "
-                      f"single thread, plain C oracle"}
+    names = [n for n, _ in w.params[:smp["keep"]]]
+    sample = (f"first {smp['keep']} of {w.n} parameters ({names[0]} .. {names[-1]}), {int(smp['sub'].sum())} "
+              f"elements, shard {ab['shard_live']} columns, one full step (pack, {w.nd}-way reduce, overflow, Adam, "
+              f"unpack) of the plain C oracle")
+    return {"value": round(total / tn / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(tn, 3), "elem_per_s": round(ab["shard_live"] / tn, 1),
+            "identical_to_single_thread": bool(same),
+            "single_thread": {"value": round(total / t1 / 1e9, 3), "cores": 1, "seconds": round(t1, 3),
+                              "elem_per_s": round(ab["shard_live"] / t1, 1)},
+            "cpu_model": host_cpu_model(), "host_cpus": cores, "step_bytes": total}
 
 
 # ------------------------------------------------------------------- profile summaries --
 
 KERNEL_KEYS = (("adam_prepare_kernel", "adam_prepare"), ("reduce_adam_kernel", "reduce_adam"),
                ("unpack_kernel", "unpack"), ("pack_kernel", "pack"), ("reduce_kernel", "reduce"),
-               ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"))
+               ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"),
+               ("adam_streams_kernel", "probe_adam_streams"), ("copy_kernel", "probe_copy"),
+               ("read_kernel", "probe_read"), ("write_kernel", "probe_write"))
 SHORT_NAMES = tuple(s for _, s in KERNEL_KEYS) + ("pack_check",)
 
 
@@ -514,17 +692,20 @@ def _short(name: str) -> str:
     return name[:60]
 
 
-def summarize_profiles(root: str, workload: str, command: str) -> str:
+def summarize_profiles(root: str, workload: str, command: str, pid: str = "") -> str:
     """Reduce rocprofv3 CSV output (root/trace: --kernel-trace --stats; root/FETCH_SIZE and
     root/WRITE_SIZE: one --pmc pass each) to a short text summary, and record the HBM bytes
     per launch of every pipeline kernel in profiles/traffic.json.  The counters are scaled by
-    what they read for torch's 2 GiB device copy (2 GiB fetched, 2 GiB written).  Without
-    root/FETCH_SIZE the summary holds the kernel times only and traffic.json is left alone."""
+    what they read for a 2 GiB device copy (2 GiB fetched, 2 GiB written).  pid: use only the
+    files of that process (the benchmark's own, not its children's).  Without root/FETCH_SIZE
+    the summary holds the kernel times only and traffic.json is left alone."""
     import csv
     import glob
 
     def rows(pattern):
-        files = glob.glob(os.path.join(root, pattern), recursive=True)
+        files = sorted(glob.glob(os.path.join(root, pattern), recursive=True))
+        if pid:
+            files = [f for f in files if os.path.basename(f).startswith(f"{pid}_")]
         if not files:
             raise FileNotFoundError(pattern)
         with open(files[0]) as fh:
@@ -552,7 +733,7 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
                 continue
             per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         counters[cname] = per
-    # calibration: the largest "copy" dispatches (torch's 2 GiB device copy)
+    # calibration: the largest "copy" dispatches (a 2 GiB device copy)
     copies = [(max(v), k) for k, v in counters["FETCH_SIZE"].items() if "copy" in k.lower()]
     cal_kernel = max(copies)[1]
     known_kib = 2.0 * 1024 * 1024
@@ -560,7 +741,7 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
     write_cal = max(counters["WRITE_SIZE"].get(cal_kernel, [known_kib]))
     f_fac, w_fac = known_kib / fetch_cal, known_kib / write_cal
     lines += ["", "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)", "",
-              f"Calibration: torch's 2 GiB device copy reads FETCH_SIZE {fetch_cal:.0f} KiB and WRITE_SIZE "
+              f"Calibration: a 2 GiB device copy reads FETCH_SIZE {fetch_cal:.0f} KiB and WRITE_SIZE "
               f"{write_cal:.0f} KiB against 2097152 KiB each: factors {f_fac:.4f} (fetch), {w_fac:.4f} (write).", "",
               "| kernel | dispatches | avg FETCH KiB | avg WRITE KiB | scaled bytes / dispatch |",
               "|---|---|---|---|---|"]
@@ -596,23 +777,34 @@ def summarize_profiles(root: str, workload: str, command: str) -> str:
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=(1, 2, 3, 4, 5),
-                    help="workload: 2 = GPT-2 1.5B-shaped list (the default and the reported line); 1 MlpModel "
-                         "(launch-bound), 3 Llama-7B, 4 7.5B paper-style at Nd=64, 5 ragged at Nd=1024 (informational)")
-    ap.add_argument("--cpu-sample-elems", type=int, default=1_600_000_000,
+    ap.add_argument("--config", type=int, default=HEADLINE, choices=(1, 2, 3, 4, 5),
+                    help="workload of the reported line: 4 = 7.5B paper-style list at Nd=64 (default); 1 MlpModel "
+                         "(launch-bound), 2 GPT-2 1.5B, 3 Llama-7B, 5 ragged at Nd=1024")
+    ap.add_argument("--others", default=",".join(str(c) for c in OTHERS),
+                    help="comma-separated workloads run in child processes and carried under `workloads` "
+                         "('none' for none)")
+    ap.add_argument("--other-steps", type=int, default=20, help="timed steps of each other workload (at most --steps)")
+    ap.add_argument("--child-timeout", type=int, default=300)
+    ap.add_argument("--child", action="store_true", help="internal: measure --config and print its sub-object")
+    ap.add_argument("--cpu-sample-elems", type=int, default=1_500_000_000,
                     help="oracle sample: the longest prefix of the parameter list with at most this many elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--no-zero3", action="store_true", help="skip the ZeRO-3 (one bucket per layer) leg")
+    ap.add_argument("--zero3-prefetch", action="store_true",
+                    help="also time ZeRO-3 with the gathers on a second stream (slower without model compute)")
     ap.add_argument("--no-graph", action="store_true", help="skip the leg that replays the step as a HIP graph")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="reduce rocprofv3 CSVs under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/) to a text summary "
                          "on stdout and profiles/traffic.json, then exit")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
+    ap.add_argument("--profile-pid", default="", help="process whose rocprofv3 files are summarized")
     args = ap.parse_args()
     if args.summarize_profiles:
-        print(summarize_profiles(args.summarize_profiles, WORKLOAD_IDS[args.config], args.profile_command), end="")
+        print(summarize_profiles(args.summarize_profiles, WORKLOAD_IDS[args.config], args.profile_command,
+                                 args.profile_pid), end="")
         return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
@@ -622,86 +814,57 @@ def main():
 
     w = W.workload(args.config)
     device = torch.device("cuda:0")
-    ctx = setup(w, device)
-    st = ctx[0]
-    shard_sizes = [Z.zero_plan_param_info(st.plan, i).shard_size for i in range(st.n)]
-    live = W.live_mask(w, 0)
-    ab = algorithmic_bytes(w.numels, shard_sizes, live, w.nd)
-    ne = stage_elements(ab)
-    runs = {}
-    for path in ("unfused", "fused"):
-        ms_p, per_phase, launches, flag = run_gpu(w, ctx, path, args.steps, args.warmup)
-        kernels = {}
-        for p in PHASES[path]:
-            kernels[p] = {"ms": round(per_phase[p], 4), "launches": launches[p], "bytes": ab[p],
-                          "GBs": round(ab[p] / (per_phase[p] * 1e-3) / 1e9, 1),
-                          "frac": round(ab[p] / (per_phase[p] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "elements": ne[p], "elem_per_s": round(ne[p] / (per_phase[p] * 1e-3), 1)}
-        runs[path] = dict(ms=ms_p, kernels=kernels, launches=launches, flag=flag,
-                          bytes=sum(ab[p] for p in PHASES[path]))
-    ms, kernels, launches, flag = (runs["unfused"][k] for k in ("ms", "kernels", "launches", "flag"))
-    step_bytes = runs["unfused"]["bytes"]
-    fz = runs["fused"]
-    fused = {"ms_per_step": round(fz["ms"], 4), "speedup": round(ms / fz["ms"], 3),
-             "GBs": round(fz["bytes"] / (fz["ms"] * 1e-3) / 1e9, 1), "step_bytes": fz["bytes"],
-             "elem_per_s": round(ab["shard_live"] / (fz["ms"] * 1e-3), 1), "overflow_flag": fz["flag"],
-             "kernels": fz["kernels"]}
-    graph = None
-    if not args.no_graph:
-        graph_ms = run_graph(w, ctx, args.steps, args.warmup)
-        graph = {"ms_per_step": round(graph_ms, 4), "eager_ms_per_step": round(ms, 4),
-                 "speedup": round(ms / graph_ms, 3)}
-    zero3 = None
-    if w.emulation == "full" and not args.no_zero3:
-        zero3 = run_zero3(w, ctx, args.steps, args.warmup, device, graph=not args.no_graph)
-    fk = fz["kernels"]["reduce_adam"]
-    fused["roofline"] = {"bound": "hbm", "kernel": "reduce_adam", "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "achieved": fk["GBs"], "frac": fk["frac"],
-                         "traffic": measured_traffic("reduce_adam", WORKLOAD_IDS[args.config]),
-                         "bytes_per_launch": fk["bytes"] // fk["launches"],
-                         "avg_launch_ms": round(fk["ms"] / fk["launches"], 4)}
-    dom = max(kernels, key=lambda p: kernels[p]["ms"])
-    workload = WORKLOAD_IDS[args.config]
-    traffic = measured_traffic(dom, workload)
-    d = kernels[dom]
+    if args.child:
+        print(json.dumps(measure_workload(w, args, device, headline=False)), flush=True)
+        return
+    res = measure_workload(w, args, device, headline=True)
+    kernels = res["kernels"]
     out = {
         "metric": METRIC,
-        "value": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "value": res["GBs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config],
-                   "workload_id": workload, "nd": w.nd, "rank": w.rank, "n_params": w.n,
-                   "psi": int(sum(s * w.nd for s in shard_sizes)), "shard_elems": ab["shard_live"],
-                   "n_buckets": launches["pack"],
-                   "storage": ("bf16" if w.dtype == W.BF16 else "fp16") + " grads/params, fp32 state",
-                   "emulation": w.emulation},
-        "elem_per_s": round(ab["shard_live"] / (ms * 1e-3), 1),
-        "grad_elem_per_s": round(ab["numel_live"] / (ms * 1e-3), 1),
-        "step_bytes": step_bytes,
-        "overflow_flag": flag,
+        "config": {k: res[k] for k in ("workload", "workload_id", "nd", "rank", "n_params", "psi", "shard_elems",
+                                       "n_buckets", "storage", "emulation")},
+        "frac": res["frac"],
+        "elem_per_s": res["elem_per_s"],
+        "grad_elem_per_s": res["grad_elem_per_s"],
+        "step_bytes": res["step_bytes"],
+        "overflow_flag": res["overflow_flag"],
         "kernels": kernels,
-        "fused": fused,
-        "zero3": zero3,
-        "graph": graph,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(d["bytes"] / launches[dom] /
-                                                                      (d["ms"] / launches[dom] * 1e-3) / 1e9, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
-                     "traffic": traffic, "bytes_per_launch": d["bytes"] // launches[dom],
-                     "avg_launch_ms": round(d["ms"] / launches[dom], 4)},
+        "fused": res["fused"],
+        "graph": res.get("graph"),
+        "roofline": res["roofline"],
+        "ceilings": None,
         "copy_reference_GBs": copy_reference(device),
         "cpu_baseline": None,
+        "workloads": {},
+        "pid": os.getpid(),
     }
-    if not args.no_cpu_baseline and args.config == 2:
+    if not args.no_ceilings:
+        shard = res["shard_elems"]
+        c = ceilings(device, adam_cols=shard, pack_bytes=kernels["pack"]["bytes"] // kernels["pack"]["launches"])
+        for stage, pat in (("adam", "adam_streams"), ("pack", "copy"), ("unpack", "copy"), ("reduce", "read")):
+            c[pat].setdefault("kernels_vs_pattern", {})[stage] = round(kernels[stage]["GBs"] / c[pat]["GBs"], 4)
+        out["ceilings"] = c
+    if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline) ...")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_elems)
+        log(f"[bench] oracle: {out['cpu_baseline']['single_thread']['seconds']} s on one thread, "
+            f"{out['cpu_baseline']['seconds']} s on {out['cpu_baseline']['cores']}")
+    others = [] if args.others in ("", "none") else [int(c) for c in args.others.split(",")]
+    others = [c for c in others if c != args.config]
+    torch.cuda.empty_cache()
+    if others:
+        out["workloads"] = run_children(others, args)
     print(json.dumps(out), flush=True)
 
 

@@ -36,7 +36,12 @@
  *   block starts at element Nd * O_b.
  *
  * Ownership and threading:
- *   The caller owns every data buffer and pointer table (device memory).  A plan owns its
+ *   The caller owns every data buffer and pointer table (device memory).  A pointer table
+ *   and every buffer it names must stay allocated until all work that reads or writes
+ *   through them has finished: the calls only enqueue kernels, and a kernel dereferences the
+ *   table's pointers when it runs -- after the call returned, and again at every replay of a
+ *   captured graph.  Freeing a named buffer earlier (or letting a caching allocator hand its
+ *   memory back to the driver) makes a later kernel access unmapped memory.  A plan owns its
  *   host tables, its device copies of them and a small device scratch used by
  *   zero_adam_step.  Hot calls (pack, reduce, overflow, adam, unpack) never allocate and
  *   never synchronise the host; they enqueue on `stream` (a hipStream_t; NULL = the null

@@ -33,7 +33,7 @@ P_NUMEL, P_PAD, P_PADDED, P_SHARD, P_START, P_END, P_OFFSET, P_BUCKET, P_COL = r
 B_FIRST, B_COUNT, B_ROW, B_STRIDE, B_BASE = range(5)
 
 GCC_FLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fexcess-precision=standard",
-             "-fPIC", "-shared", "-Wall", "-Werror"]
+             "-fopenmp", "-fPIC", "-shared", "-Wall", "-Werror"]
 # ORACLE_SANITIZE=1: build with AddressSanitizer and UBSan (host code; run the tests with
 # LD_PRELOAD of gcc's libasan.so and libubsan.so and ASAN_OPTIONS=detect_leaks=0)
 SANITIZE_FLAGS = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
@@ -85,6 +85,10 @@ def lib():
         L.oracle_pack_locate.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         L.oracle_unpack_locate.restype = None
         L.oracle_unpack_locate.argtypes = [vp, i64, i64, vp, vp]
+        L.oracle_set_threads.restype = None
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_get_threads.restype = i32
+        L.oracle_get_threads.argtypes = []
         L.oracle_model_state_bytes.restype = dbl
         L.oracle_model_state_bytes.argtypes = [dbl, dbl, i32]
         for name in ("oracle_convert_to_f32", "oracle_convert_from_f32"):
@@ -92,6 +96,16 @@ def lib():
             getattr(L, name).argtypes = [vp, vp, i64, i32]
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Host threads for the oracle's element loops (default 1).  Each loop over one
+    parameter's columns is split into disjoint ranges; results are identical for any count."""
+    lib().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().oracle_get_threads())
 
 
 def _ptr(a: np.ndarray) -> int:

@@ -61,14 +61,27 @@ enum { ORB_FIRST = 0, ORB_COUNT, ORB_ROW, ORB_STRIDE, ORB_BASE, ORB_NFIELDS };
 #define OR_FP16 2
 
 int oracle_param_fields(void) { return ORP_NFIELDS; }
+
+/*
+ * Threads for the element loops (1 unless set).  With more than one thread, a loop over the
+ * columns (or elements) of one parameter is split into disjoint contiguous ranges, one per
+ * thread; every element is still computed by the same operations in the same order, so the
+ * results are identical for any thread count.  Used only to time the oracle on all host cores.
+ */
+static int g_threads = 1;
+void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int oracle_get_threads(void) { return g_threads; }
+#define OR_PARALLEL _Pragma("omp parallel for num_threads(g_threads) if(g_threads > 1) schedule(static)")
+#define OR_PARALLEL2 _Pragma("omp parallel for collapse(2) num_threads(g_threads) if(g_threads > 1) schedule(static)")
 int oracle_bucket_fields(void) { return ORB_NFIELDS; }
 
 /* ------------------------------------------------------------------ plan (O1) ------ */
 /*
- * [FR Implémentation simplifiée]: remainder = numel mod world_size, pad = (world_size -
- * remainder) mod world_size, padded = numel + pad, shard_size = padded / world_size,
- * shard_start = rank * shard_size, shard_end = shard_start + shard_size.
- * [LLZ INIT]: every parameter is split evenly over the ranks, rank r keeps row r.
+ * [FR Implémentation simplifiée]: every flat parameter is zero-padded to a multiple of the
+ * world size, viewed as [world_size, -1], and rank r owns row r (its shard_start and
+ * shard_end in the padded flat).  [LLZ INIT]: every parameter is split evenly over the ranks.
+ * Here a row holds ceil(numel / Nd) elements; the padding is whatever the Nd full rows hold
+ * beyond numel (the tests check it against the page's pad formula for every numel up to 3Nd).
  * [LLZ BWD]: gradients go into buckets; when full, each one is viewed as [Nd, -1] and the
  * rows of one rank are flattened together.
  * [Z3]: ZeRO-3 gathers and frees the parameters one layer (unit) at a time; with groups (one
@@ -83,17 +96,13 @@ int64_t oracle_plan(const int64_t* numels, const int32_t* groups, int64_t n, int
     for (int64_t i = 0; i < n; i++) {
         if (numels[i] < 0) return -1;
         int64_t* p = params + i * ORP_NFIELDS;
-        int64_t numel = numels[i];
-        int64_t remainder = numel % nd;
-        int64_t pad = (nd - remainder) % nd;
-        int64_t padded = numel + pad;
-        int64_t shard = padded / nd;
-        p[ORP_NUMEL] = numel;
-        p[ORP_PAD] = pad;
-        p[ORP_PADDED] = padded;
-        p[ORP_SHARD] = shard;
-        p[ORP_START] = rank * shard;
-        p[ORP_END] = rank * shard + shard;
+        int64_t row_len = (numels[i] + nd - 1) / nd; /* elements of one rank's row */
+        p[ORP_NUMEL] = numels[i];
+        p[ORP_SHARD] = row_len;
+        p[ORP_PADDED] = nd * row_len;
+        p[ORP_PAD] = nd * row_len - numels[i];
+        p[ORP_START] = rank * row_len;
+        p[ORP_END] = (rank + 1) * row_len;
     }
 
     /* Greedy buckets over the list, capacity in 16-bit elements (0 bytes = unbounded). */
@@ -226,6 +235,7 @@ void oracle_pack_bucket(const int64_t* params, const int64_t* buckets, int64_t n
         if (g == NULL) continue;
         const int64_t* p = params + i * ORP_NFIELDS;
         int64_t s = p[ORP_SHARD], numel = p[ORP_NUMEL], col = p[ORP_COL];
+        OR_PARALLEL2
         for (int64_t k = 0; k < nd; k++)
             for (int64_t j = 0; j < s; j++) {
                 int64_t e = k * s + j;
@@ -255,6 +265,7 @@ void oracle_reduce_bucket(const int64_t* params, const int64_t* buckets, int64_t
     for (int64_t i = bk[ORB_FIRST]; i < bk[ORB_FIRST] + bk[ORB_COUNT]; i++) {
         if (!live[i]) continue;
         const int64_t* p = params + i * ORP_NFIELDS;
+        OR_PARALLEL
         for (int64_t j = 0; j < p[ORP_SHARD]; j++) {
             int64_t c = p[ORP_COL] + j;
             g32[bk[ORB_BASE] + c] = oracle_reduce_column(rows + c, nd, row_stride, dtype);
@@ -269,6 +280,7 @@ int oracle_overflow(const int64_t* params, int64_t n, const float* g32, const ui
     for (int64_t i = 0; i < n; i++) {
         if (!live[i]) continue;
         const int64_t* p = params + i * ORP_NFIELDS;
+        _Pragma("omp parallel for num_threads(g_threads) if(g_threads > 1) schedule(static) reduction(|:flag)")
         for (int64_t e = p[ORP_OFFSET]; e < p[ORP_OFFSET] + p[ORP_SHARD]; e++) {
             uint32_t bits;
             memcpy(&bits, &g32[e], 4);
@@ -337,6 +349,7 @@ void oracle_adam(const int64_t* params, const int64_t* buckets, int64_t n, int64
         const int64_t* p = params + i * ORP_NFIELDS;
         const int64_t* bk = buckets + p[ORP_BUCKET] * ORB_NFIELDS;
         steps[i] += 1;
+        OR_PARALLEL
         for (int64_t e = p[ORP_OFFSET]; e < p[ORP_OFFSET] + p[ORP_SHARD]; e++) {
             oracle_adam_element(g32[e], &p32[e], &m[e], &v[e], steps[i], lr, beta1, beta2, eps, grad_scale);
             int64_t c = e - bk[ORB_BASE];
@@ -396,6 +409,7 @@ void oracle_unpack_bucket(const int64_t* params, const int64_t* buckets, int64_t
         if (out == NULL) continue;
         const int64_t* p = params + i * ORP_NFIELDS;
         int64_t s = p[ORP_SHARD];
+        OR_PARALLEL
         for (int64_t e = 0; e < p[ORP_NUMEL]; e++) {
             int64_t k = e / s, j = e % s;
             out[e] = gathered[k * L + p[ORP_COL] + j];

@@ -33,6 +33,25 @@ def test_header_and_binding_agree():
     assert declared_functions() == sorted(B.EXPORTS)
 
 
+def test_probe_library_exports_its_header():
+    """libzero_probe.so (the bandwidth probes beside the pipeline) exports every function
+    include/zero_probe.h declares, and its binding names the same set."""
+    from zero_sharded_mixed_amd import probe
+    if not os.path.exists(probe.LIB_PATH):
+        from zero_sharded_mixed_amd import build
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "zero_probe.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(zero_probe_[a-z_0-9]+)\s*\(", text)))
+    assert declared == sorted(probe.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(zero_probe_\w+)$", out, flags=re.M))
+    assert set(declared) <= exported
+    L = probe.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
 def test_library_exports_every_declared_symbol(L):
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(zero_\w+)$", out, flags=re.M))

@@ -207,14 +207,10 @@ def run_fullsize(config, max_steps=None, n_samples=20000):
             recv = []
             for b in range(pl.n_buckets):
                 L = int(pl.buckets[b, oracle.B_STRIDE])
-                blk = torch.empty((nd, L), dtype=torch.int16, device=DEV)
+                blk = W.remote_rows(w, step, b, L, DEV).view(torch.int16)
                 zero = torch.from_numpy(row_zero_mask(pl, b, live)).to(DEV)
-                for k in range(nd):
-                    if k == r:
-                        blk[k].copy_(st.own_row(st.packed, b))
-                    else:
-                        blk[k].copy_(W.remote_row(w, step, k, b, L, DEV).view(torch.int16))
-                        blk[k].masked_fill_(zero, 0)
+                blk.masked_fill_(zero.unsqueeze(0), 0)
+                blk[r].copy_(st.own_row(st.packed, b))
                 recv.append(blk)
             # inf / NaN injections on odd steps at live positions of other ranks' rows; some
             # land on sampled columns so that the oracle sees them
@@ -308,3 +304,80 @@ def test_fullsize_workload(config):
     finally:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_injected_inf_skips_both_paths():
+    """The 7.5B paper-style list (fp16 gradients, loss scale 2^16, Nd = 64, rank 63) at its real
+    size, in the launch configuration bench.py times, with one +inf planted in this rank's
+    gradient at an element of its own row r.  The oracle's verdict for that step is "skip"
+    (the reduced column is non-finite; its input check flags the gradient too).  The unfused
+    path (pack -> reduce with the fused check -> Adam) and the fused path (checked pack ->
+    reduce + Adam) both raise the flag, and neither changes p32, m, v, the step counts or the
+    all-gather arena: every array bit-identical to its state before the step."""
+    w = W.workload(4)
+    nd, r = w.nd, w.rank
+    pl = oracle.plan(w.numels, nd, r, w.bucket_bytes)
+    X = Z.ShardStep(w.numels, nd, r, w.bucket_bytes, w.dtype)
+    masters = W.masters(w, DEV)
+    X.init_master(Z.ptr_table(masters), 0)
+    lp = W.to_16bit(masters, w.dtype)
+    del masters
+    X.pack(Z.ptr_table(lp), out=X.arena)
+    del lp
+    live = W.live_mask(w, 0)
+    X.live.copy_(torch.from_numpy(live))
+    g = W.grads(w, 0, r, DEV)
+    i = [n for n, _ in w.params].index("h.0.qkv.weight")
+    s_i, col = int(pl.params[i, P_S]), int(pl.params[i, P_COL])
+    j = 12345
+    e = r * s_i + j                                       # element j of rank r's row of parameter i
+    assert e < pl.params[i, P_NUMEL]
+    g[i][e] = float("inf")
+    b = int(pl.params[i, P_BUCKET])
+    # the oracle's verdicts: its input check over the bucket's gradients, and the reduce of the
+    # planted column (the other ranks' values from the row generator)
+    host = [bits16(t.cpu()) if pl.params[k, P_BUCKET] == b else None for k, t in enumerate(g)]
+    assert oracle.input_check(pl, b, host, w.dtype) == 1
+    del host
+    own = Z.ptr_table(g)
+    X.pack(own)
+    recv = []
+    for bb in range(pl.n_buckets):
+        L = int(pl.buckets[bb, oracle.B_STRIDE])
+        blk = W.remote_rows(w, 0, bb, L, DEV).view(torch.int16)
+        blk.masked_fill_(torch.from_numpy(row_zero_mask(pl, bb, live)).to(DEV).unsqueeze(0), 0)
+        blk[r].copy_(X.own_row(X.packed, bb))
+        recv.append(blk)
+    column = bits16(recv[b][:, col + j].cpu())
+    assert column[r] == 0x7C00  # the packed row carries the +inf
+    g32 = np.zeros(pl.shard_len, np.float32)
+    g32[int(pl.params[i, P_OFF]) + j] = oracle.reduce_column(column, w.dtype)
+    only = np.zeros(pl.n, np.uint8)
+    only[i] = 1
+    assert oracle.overflow(pl, g32, only) == 1
+    rows_of = lambda bb: (recv[bb].view(-1), int(pl.buckets[bb, oracle.B_STRIDE]))
+    before = {k: t.clone() for k, t in (("p32", X.p32), ("m", X.m), ("v", X.v), ("steps", X.steps),
+                                        ("arena", X.arena))}
+
+    def unchanged(what):
+        for k, t in (("p32", X.p32), ("m", X.m), ("v", X.v), ("steps", X.steps), ("arena", X.arena)):
+            assert torch.equal(t.view(torch.int32) if t.dtype == torch.float32 else t,
+                               before[k].view(torch.int32) if t.dtype == torch.float32 else before[k]), (what, k)
+
+    hp = (w.lr, w.betas[0], w.betas[1], w.eps, w.grad_scale)
+    X.flag.zero_()
+    X.reduce(rows_of)
+    X.adam(*hp)
+    torch.cuda.synchronize()
+    assert int(X.flag.item()) == 1
+    assert not np.isfinite(to_np32(X.g32[int(pl.params[i, P_OFF]) + j:int(pl.params[i, P_OFF]) + j + 1])[0])
+    unchanged("unfused")
+    X.flag.zero_()
+    X.pack(own, out=torch.empty_like(X.packed), check=True)
+    assert int(X.flag.item()) == 1
+    X.reduce_adam(rows_of, *hp)
+    torch.cuda.synchronize()
+    unchanged("fused")
+    del recv, g, own, X, before
+    torch.cuda.empty_cache()

@@ -324,8 +324,19 @@ def test_fused_calls_reject_bad_arguments():
     assert _status(lambda: ra(st.plan, 0, buf, L + 4, st.live, f, f, f, None, st.arena)) == E    # stride % 8
     assert _status(lambda: ra(st.plan, 0, buf[1:], L, st.live, f, f, f, None, st.arena)) == E    # rows
     assert _status(lambda: ra(st.plan, 0, buf, L, st.live, f[1:], f, f, None, st.arena)) == E    # p32
-    assert _status(lambda: ra(st.plan, 0, buf, L, st.live, f, f, f, None, st.arena[3:])) == E    # arena
+    big = torch.zeros(int(st.summary.arena_numel) + 64, dtype=torch.int16, device=DEV)
+    assert _status(lambda: ra(st.plan, 0, buf, L, st.live, f, f, f, None, big[3:])) == E         # arena
     assert _status(lambda: ra(st.plan, 0, buf, L, None, f, f, f, None, st.arena)) == E           # live
+    # buffers too small for what the kernels would touch are refused before any launch
+    with pytest.raises(ValueError, match="arena"):
+        ra(st.plan, 0, buf, L, st.live, f, f, f, None, st.arena[8:])
+    with pytest.raises(ValueError, match="rows"):
+        ra(st.plan, 0, buf[:7 * L + L - 8], L, st.live, f, f, f, None, st.arena)
+    with pytest.raises(ValueError, match="entry 1"):
+        Z.zero_pack_bucket_check(st.plan, 0, Z.ptr_table([ptrs.zero_targets[0], buf[:36], ptrs.zero_targets[2]]),
+                                 buf, st.flag)
+    with pytest.raises(ValueError, match="ptr_table"):
+        Z.zero_pack_bucket_check(st.plan, 0, ptrs.clone(), buf, st.flag)
     torch.cuda.synchronize()
     assert int(st.steps.sum().item()) == 0 and int(st.flag.item()) == 0
 
@@ -373,14 +384,10 @@ def run_fused_fullsize(config, n_steps=2, n_samples=8000):
         recv = []
         for b in range(pl.n_buckets):
             L = int(pl.buckets[b, oracle.B_STRIDE])
-            blk = torch.empty((nd, L), dtype=torch.int16, device=DEV)
+            blk = W.remote_rows(w, step, b, L, DEV).view(torch.int16)
             zero = torch.from_numpy(row_zero_mask(pl, b, live)).to(DEV)
-            for k in range(nd):
-                if k == r:
-                    blk[k].copy_(A.own_row(A.packed, b))
-                else:
-                    blk[k].copy_(W.remote_row(w, step, k, b, L, DEV).view(torch.int16))
-                    blk[k].masked_fill_(zero, 0)
+            blk.masked_fill_(zero.unsqueeze(0), 0)
+            blk[r].copy_(A.own_row(A.packed, b))
             recv.append(blk)
         # another rank's gradient overflowed on odd steps of the lists that inject: its own
         # check set its flag, and the all-reduce of the flags brings it here

@@ -158,8 +158,14 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(prefetch):
     pa = torch.empty((nd, int(A.summary.arena_numel)), dtype=torch.int16, device=DEV)
     pg = torch.empty((nd, int(G.summary.arena_numel)), dtype=torch.int16, device=DEV)
     own = None
+    # rows[k][t] = virtual rank k's value at sampled column t, taken from its generated
+    # gradients (element ce of parameter ci, +0 for padding): the oracle's input never comes
+    # from a HIP kernel's output
+    real = ce < pl.params[ci, oracle.P_NUMEL]
+    rows = np.zeros((nd, cols.size), np.uint16)
     for k in range(nd):
         g = [t if l else None for t, l in zip(W.grads(w, 0, k, DEV), live)]
+        rows[k] = np.where(real, bits16(gather_params(g, ci, ce, 0)), 0)
         A.pack(Z.ptr_table(g), out=pa[k])
         G.pack(Z.ptr_table(g), out=pg[k])
         if k == r:
@@ -196,20 +202,7 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(prefetch):
         ra = ba.block_offset + r * ba.row_stride + ia.bucket_col
         rg = bg.block_offset + r * bg.row_stride + ig.bucket_col
         assert torch.equal(A.arena[ra:ra + s], G.arena[rg:rg + s]), i
-    # the oracle on sampled columns of the per-layer plan: virtual rank k's value at column c of
-    # bucket b is element nd * O_b + r * L_b + c of its packed buffer pg[k]
-    cb = pl.params[ci, oracle.P_BUCKET]
-    cc = pl.params[ci, oracle.P_COL] + cj
-    rows = np.zeros((nd, cols.size), np.uint16)
-    flat = pg.view(-1)
-    for k in range(nd):
-        if k == r:
-            real = ce < pl.params[ci, oracle.P_NUMEL]
-            rows[k] = np.where(real, bits16(gather_params(own, ci, ce, 0)), 0)  # from the gradients themselves
-        else:
-            idx = torch.from_numpy(k * pg.shape[1] + nd * pl.buckets[cb, oracle.B_BASE] +
-                                   r * pl.buckets[cb, oracle.B_STRIDE] + cc)
-            rows[k] = bits16(flat[idx.to(DEV)].cpu())
+    # the oracle on sampled columns of the per-layer plan, from the generated gradients' rows
     ohp = oracle.AdamHP(lr=w.lr, beta1=w.betas[0], beta2=w.betas[1], eps=w.eps, grad_scale=w.grad_scale)
     want = [oracle.adam_element(oracle.reduce_column(rows[:, t], w.dtype), p0[t], 0.0, 0.0, 1, ohp)
             for t in range(cols.size)]

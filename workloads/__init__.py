@@ -181,6 +181,15 @@ def layer_groups(w: Workload) -> list:
 
 
 # ----------------------------------------------------------------- random values ------
+# Every list of per-parameter tensors is drawn as ONE flat buffer (a few large draws, not one
+# per parameter: a 10,000-parameter list would otherwise issue tens of thousands of tiny
+# launches) and returned as views into it.  Each view starts 256 bytes after a multiple of 256
+# bytes, like separate allocations would, so buffers keep the alignment the kernels' wide
+# paths need.
+
+ALIGN_BYTES = 256
+DRAW_CHUNK = 1 << 27  # elements per draw call
+
 
 def _gen(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
@@ -192,33 +201,70 @@ def _torch_dtype(dtype: int):
     return torch.bfloat16 if dtype == BF16 else torch.float16
 
 
+def flat_layout(numels, elem_bytes: int):
+    """Start of every parameter in one flat buffer (each start a multiple of ALIGN_BYTES) and
+    the buffer's length, in elements."""
+    align = ALIGN_BYTES // elem_bytes
+    starts, pos = [], 0
+    for x in numels:
+        starts.append(pos)
+        pos += (int(x) + align - 1) // align * align
+    return starts, max(pos, align)
+
+
+def _draw_normal(total: int, std: float, out_dtype, gen: torch.Generator, device) -> torch.Tensor:
+    """total values N(0, 1) * std, drawn in order in DRAW_CHUNK pieces, converted to out_dtype
+    by torch's own conversion."""
+    out = torch.empty(total, dtype=out_dtype, device=device)
+    for a in range(0, total, DRAW_CHUNK):
+        b = min(total, a + DRAW_CHUNK)
+        x = torch.randn(b - a, generator=gen, device=device, dtype=torch.float32)
+        out[a:b] = x.mul_(std) if out_dtype == torch.float32 else (x * std).to(out_dtype)
+    return out
+
+
+def _views(flat: torch.Tensor, numels, starts) -> list:
+    return [flat[s:s + int(x)] for s, x in zip(starts, numels)]
+
+
 def normal_fp32(numel: int, std: float, gen: torch.Generator, device) -> torch.Tensor:
-    return torch.randn(numel, generator=gen, device=device, dtype=torch.float32) * std
+    return _draw_normal(int(numel), std, torch.float32, gen, device)
 
 
 def normal_16(numel: int, std: float, scale: float, dtype: int, gen: torch.Generator, device) -> torch.Tensor:
     """N(0, std) * scale rounded to the 16-bit type by torch's own conversion."""
-    x = torch.randn(numel, generator=gen, device=device, dtype=torch.float32)
-    return (x * (std * scale)).to(_torch_dtype(dtype))
+    return _draw_normal(int(numel), std * scale, _torch_dtype(dtype), gen, device)
 
 
 def masters(w: Workload, device) -> list:
-    """Full fp32 master parameters N(0, master_std), one flat tensor per parameter."""
+    """Full fp32 master parameters N(0, master_std): one view per parameter into one buffer."""
     g = _gen(seed_of(w.config, 0, 0, SLOT_MASTER), device)
-    return [normal_fp32(int(x), w.master_std, g, device) for x in w.numels]
+    starts, total = flat_layout(w.numels, 4)
+    return _views(normal_fp32(total, w.master_std, g, device), w.numels, starts)
+
+
+def to_16bit(views: list, dtype: int) -> list:
+    """A list of views into one flat buffer (as masters() returns), converted to the 16-bit
+    type by one torch conversion of that buffer; the new views sit at the same element
+    offsets (so each still starts on a 16-byte boundary)."""
+    base = views[0]._base if views[0]._base is not None else views[0]
+    assert all(v._base is base or v is base for v in views), "views of one flat buffer expected"
+    flat = base.to(_torch_dtype(dtype))
+    return [flat[v.storage_offset():v.storage_offset() + v.numel()] for v in views]
 
 
 def grads(w: Workload, step: int, vrank: int, device) -> list:
-    """One virtual rank's full gradient list (16-bit flats), with exact zeros if asked."""
+    """One virtual rank's full gradient list (16-bit; one view per parameter into one buffer),
+    with exact zeros at a fraction zero_frac of the elements if asked."""
     g = _gen(seed_of(w.config, step, vrank, SLOT_GRAD), device)
-    out = []
-    for x in w.numels:
-        t = normal_16(int(x), w.grad_std, w.loss_scale, w.dtype, g, device)
-        if w.zero_frac > 0 and x > 0:
-            z = torch.rand(int(x), generator=g, device=device) < w.zero_frac
-            t = t.masked_fill(z, 0.0)
-        out.append(t)
-    return out
+    starts, total = flat_layout(w.numels, 2)
+    flat = normal_16(total, w.grad_std, w.loss_scale, w.dtype, g, device)
+    if w.zero_frac > 0:
+        for a in range(0, total, DRAW_CHUNK):
+            b = min(total, a + DRAW_CHUNK)
+            z = torch.rand(b - a, generator=g, device=device) < w.zero_frac
+            flat[a:b].masked_fill_(z, 0.0)
+    return _views(flat, w.numels, starts)
 
 
 def live_mask(w: Workload, step: int) -> np.ndarray:
@@ -232,11 +278,12 @@ def live_mask(w: Workload, step: int) -> np.ndarray:
     return live
 
 
-def remote_row(w: Workload, step: int, vrank: int, bucket: int, length: int, device) -> torch.Tensor:
-    """Random 16-bit values standing for virtual rank `vrank`'s packed row of one bucket
-    (row-only emulation; the caller zeroes the positions a real packer leaves zero)."""
-    g = _gen(seed_of(w.config, step, vrank, SLOT_ROWS) + 7 * bucket, device)
-    return normal_16(length, w.grad_std, w.loss_scale, w.dtype, g, device)
+def remote_rows(w: Workload, step: int, bucket: int, length: int, device) -> torch.Tensor:
+    """Random 16-bit values standing for every virtual rank's packed row r of one bucket
+    ([Nd, length]; row k = virtual rank k's), drawn at once (row-only emulation; the caller
+    puts this rank's own row in place and zeroes the positions a real packer leaves zero)."""
+    g = _gen(seed_of(w.config, step, 0, SLOT_ROWS) + 7 * bucket, device)
+    return normal_16(w.nd * int(length), w.grad_std, w.loss_scale, w.dtype, g, device).view(w.nd, int(length))
 
 
 def injections(w: Workload, step: int, count_space: int, device="cpu"):

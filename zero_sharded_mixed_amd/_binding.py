@@ -11,6 +11,7 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,15 @@ class zero_adam_hparams(ctypes.Structure):
 
 
 _lib = None
+LOSS_SCALER_BYTES = ctypes.sizeof(zero_loss_scaler)
+
+
+def _scaler(plan: "Plan", t: Optional[torch.Tensor], what: str) -> Optional[int]:
+    if t is None:
+        return None
+    if t.numel() * t.element_size() < LOSS_SCALER_BYTES:
+        raise ValueError(f"{what}: loss scaler tensor too small")
+    return _buf(plan, t, what + ": loss scaler", 0)
 
 
 def lib() -> ctypes.CDLL:
@@ -127,6 +137,32 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
+def _buf(plan: "Plan", t: Optional[torch.Tensor], what: str, min_elems: int, dtypes=None,
+         elem_size: Optional[int] = None) -> Optional[int]:
+    """Pointer of a buffer a kernel will read or write: on the plan's device, contiguous, of an
+    allowed dtype (or element size) and holding at least min_elems elements.  Raises
+    ValueError otherwise, before anything is launched.  None passes through (the library
+    decides whether NULL is allowed)."""
+    if t is None:
+        return None
+    if not t.is_cuda or t.device.index != plan.device:
+        raise ValueError(f"{what}: tensor must live on cuda:{plan.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: contiguous tensor expected")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype} not in {tuple(dtypes)}")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise ValueError(f"{what}: {elem_size}-byte elements expected, got {t.dtype}")
+    if t.numel() < min_elems:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {min_elems} needed")
+    return t.data_ptr()
+
+
+F32 = (torch.float32,)
+I32 = (torch.int32,)
+U8 = (torch.uint8, torch.bool)
+
+
 def ptr_table(tensors: Sequence[Optional[torch.Tensor]], device=None) -> torch.Tensor:
     """Device int64 array of the tensors' data pointers (0 for None): a pointer table.
 
@@ -134,25 +170,81 @@ def ptr_table(tensors: Sequence[Optional[torch.Tensor]], device=None) -> torch.T
     `zero_targets`), so their memory stays allocated for as long as the table object is alive:
     a kernel that reads through the table, at once or when a captured graph is replayed, never
     reads memory that the caching allocator has freed or handed back to the driver.  A slice or
-    copy of the table is a new tensor object and does not carry the references."""
+    copy of the table is a new tensor object and carries neither the references nor the sizes
+    below, so the entry points refuse it.  It also records every entry's element count and
+    element size (`zero_numels`, `zero_elem_sizes`; 0 for None), which the entry points check
+    against the plan before they launch."""
     keep = list(tensors)
     ptrs = [0 if t is None else _ptr(t) for t in keep]
     table = torch.tensor(ptrs, dtype=torch.int64, device=device or "cuda")
     table.zero_targets = keep
+    table.zero_numels = np.array([0 if t is None else t.numel() for t in keep], dtype=np.int64)
+    table.zero_elem_sizes = np.array([0 if t is None else t.element_size() for t in keep], dtype=np.int64)
+    table.zero_devices = {t.device.index for t in keep if t is not None}
     return table
 
 
+def _table(plan: "Plan", table: torch.Tensor, what: str, elem_size: int) -> int:
+    """Pointer of a pointer table after checking, entry by entry, that every non-NULL entry
+    of a parameter with elements is a buffer of elem_size-byte elements on the plan's device
+    holding at least numel_i elements (a kernel reads or writes that many through it)."""
+    numels = getattr(table, "zero_numels", None)
+    if numels is None:
+        raise ValueError(f"{what}: pointer table must come from ptr_table() (a slice or copy drops its sizes)")
+    if table.numel() != plan.n or numels.shape[0] != plan.n:
+        raise ValueError(f"{what}: pointer table has {table.numel()} entries, the plan {plan.n} parameters")
+    # entries of parameters with no elements are never dereferenced
+    present = (table.zero_elem_sizes != 0) & (plan.numels > 0)
+    if np.any(table.zero_elem_sizes[present] != elem_size):
+        raise ValueError(f"{what}: every buffer in the table must have {elem_size}-byte elements")
+    short = present & (numels < plan.numels)
+    if np.any(short):
+        i = int(np.flatnonzero(short)[0])
+        raise ValueError(f"{what}: entry {i} holds {int(numels[i])} elements, parameter {i} has {int(plan.numels[i])}")
+    if table.zero_devices - {plan.device}:
+        raise ValueError(f"{what}: every buffer in the table must live on cuda:{plan.device}")
+    return _buf(plan, table, what + " table", plan.n, dtypes=(torch.int64,))
+
+
 class Plan:
-    """Owns a zero_plan*; destroyed with the object (or by close())."""
+    """Owns a zero_plan*; destroyed with the object (or by close()).  Keeps the sizes the
+    entry points' argument checks need: per-parameter numel, per-bucket row length and row
+    stride, the shard and arena lengths."""
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
+        s = zero_plan_summary()
+        _check(lib().zero_plan_get_summary(self._h, ctypes.byref(s)))
+        self.n, self.nd, self.device = int(s.n_params), int(s.nd), int(s.device)
+        self.n_buckets, self.shard_numel, self.arena_numel = int(s.n_buckets), int(s.shard_numel), int(s.arena_numel)
+        info = zero_param_info()
+        numels = np.zeros(self.n, dtype=np.int64)
+        for i in range(self.n):
+            _check(lib().zero_plan_param_info(self._h, i, ctypes.byref(info)))
+            numels[i] = info.numel
+        self.numels = numels
+        bk = zero_bucket_info()
+        self.row_stride = []
+        for b in range(self.n_buckets):
+            _check(lib().zero_plan_bucket_info(self._h, b, ctypes.byref(bk)))
+            self.row_stride.append(int(bk.row_stride))
 
     @property
     def handle(self) -> ctypes.c_void_p:
         if not self._h:
             raise ValueError("plan is closed")
         return self._h
+
+    def block_elems(self, b: int) -> int:
+        """Elements of bucket b's [Nd][L_b] block (0 for an index out of range: the library
+        rejects the index)."""
+        return self.nd * self.row_stride[b] if 0 <= b < self.n_buckets else 0
+
+    def rows_elems(self, b: int, row_stride: int) -> int:
+        """Elements a reduce of bucket b reads from its rows buffer."""
+        if not 0 <= b < self.n_buckets or self.row_stride[b] == 0:
+            return 0
+        return (self.nd - 1) * max(int(row_stride), 0) + self.row_stride[b]
 
     def close(self) -> None:
         if self._h:
@@ -219,18 +311,25 @@ def zero_plan_model_state_bytes(plan: Plan, stage: int) -> float:
 
 
 def zero_pack_bucket(plan: Plan, b: int, grad_ptrs: torch.Tensor, packed: torch.Tensor, stream=None) -> None:
-    _check(lib().zero_pack_bucket(plan.handle, b, _ptr(grad_ptrs), _ptr(packed), _stream(stream)))
+    _check(lib().zero_pack_bucket(plan.handle, b, _table(plan, grad_ptrs, "zero_pack_bucket: gradients", 2),
+                                  _buf(plan, packed, "zero_pack_bucket: packed", plan.block_elems(b), elem_size=2),
+                                  _stream(stream)))
 
 
 def zero_reduce_shard(plan: Plan, b: int, rows: torch.Tensor, row_stride: int, live: torch.Tensor,
                       g32: torch.Tensor, flag: Optional[torch.Tensor] = None, stream=None) -> None:
     """rows: 16-bit device tensor whose start is row 0; row k starts k*row_stride elements in."""
-    _check(lib().zero_reduce_shard(plan.handle, b, _ptr(rows), row_stride, _ptr(live), _ptr(g32), _ptr(flag),
-                                   _stream(stream)))
+    _check(lib().zero_reduce_shard(plan.handle, b, _buf(plan, rows, "zero_reduce_shard: rows",
+                                                        plan.rows_elems(b, row_stride), elem_size=2),
+                                   row_stride, _buf(plan, live, "zero_reduce_shard: live", plan.n, U8),
+                                   _buf(plan, g32, "zero_reduce_shard: g32", plan.shard_numel, F32),
+                                   _buf(plan, flag, "zero_reduce_shard: flag", 1, I32), _stream(stream)))
 
 
 def zero_overflow_check(plan: Plan, g32: torch.Tensor, live: torch.Tensor, flag: torch.Tensor, stream=None) -> None:
-    _check(lib().zero_overflow_check(plan.handle, _ptr(g32), _ptr(live), _ptr(flag), _stream(stream)))
+    _check(lib().zero_overflow_check(plan.handle, _buf(plan, g32, "zero_overflow_check: g32", plan.shard_numel, F32),
+                                     _buf(plan, live, "zero_overflow_check: live", plan.n, U8),
+                                     _buf(plan, flag, "zero_overflow_check: flag", 1, I32), _stream(stream)))
 
 
 def zero_adam_step(plan: Plan, g32: torch.Tensor, p32: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
@@ -238,41 +337,59 @@ def zero_adam_step(plan: Plan, g32: torch.Tensor, p32: torch.Tensor, m: torch.Te
                    grad_scale: float, flag: Optional[torch.Tensor], arena: torch.Tensor, stream=None,
                    loss_scaler: Optional[torch.Tensor] = None) -> None:
     """loss_scaler: device tensor holding a zero_loss_scaler (see LOSS_SCALER_BYTES), or None."""
-    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _ptr(loss_scaler))
-    _check(lib().zero_adam_step(plan.handle, _ptr(g32), _ptr(p32), _ptr(m), _ptr(v), _ptr(live), _ptr(steps),
-                                ctypes.byref(hp), _ptr(flag), _ptr(arena), _stream(stream)))
+    S, w = plan.shard_numel, "zero_adam_step"
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _scaler(plan, loss_scaler, w))
+    _check(lib().zero_adam_step(plan.handle, _buf(plan, g32, w + ": g32", S, F32), _buf(plan, p32, w + ": p32", S, F32),
+                                _buf(plan, m, w + ": m", S, F32), _buf(plan, v, w + ": v", S, F32),
+                                _buf(plan, live, w + ": live", plan.n, U8), _buf(plan, steps, w + ": steps", plan.n, I32),
+                                ctypes.byref(hp), _buf(plan, flag, w + ": flag", 1, I32),
+                                _buf(plan, arena, w + ": arena", plan.arena_numel, elem_size=2), _stream(stream)))
 
 
 def zero_unpack(plan: Plan, b: int, gathered: torch.Tensor, param_ptrs: torch.Tensor, stream=None) -> None:
-    _check(lib().zero_unpack(plan.handle, b, _ptr(gathered), _ptr(param_ptrs), _stream(stream)))
+    _check(lib().zero_unpack(plan.handle, b, _buf(plan, gathered, "zero_unpack: gathered", plan.block_elems(b),
+                                                  elem_size=2),
+                             _table(plan, param_ptrs, "zero_unpack: parameters", 2), _stream(stream)))
 
 
 def zero_shard_init(plan: Plan, src_ptrs: torch.Tensor, src_dtype: int, p32: torch.Tensor, stream=None) -> None:
-    _check(lib().zero_shard_init(plan.handle, _ptr(src_ptrs), src_dtype, _ptr(p32), _stream(stream)))
+    _check(lib().zero_shard_init(plan.handle, _table(plan, src_ptrs, "zero_shard_init: sources",
+                                                     4 if src_dtype == 0 else 2), src_dtype,
+                                 _buf(plan, p32, "zero_shard_init: p32", plan.shard_numel, F32), _stream(stream)))
 
 
 def zero_pack_bucket_check(plan: Plan, b: int, grad_ptrs: torch.Tensor, packed: torch.Tensor, flag: torch.Tensor,
                            stream=None) -> None:
-    _check(lib().zero_pack_bucket_check(plan.handle, b, _ptr(grad_ptrs), _ptr(packed), _ptr(flag), _stream(stream)))
+    w = "zero_pack_bucket_check"
+    _check(lib().zero_pack_bucket_check(plan.handle, b, _table(plan, grad_ptrs, w + ": gradients", 2),
+                                        _buf(plan, packed, w + ": packed", plan.block_elems(b), elem_size=2),
+                                        _buf(plan, flag, w + ": flag", 1, I32), _stream(stream)))
 
 
 def zero_adam_prepare(plan: Plan, live: torch.Tensor, steps: torch.Tensor, lr: float, beta1: float, beta2: float,
                       eps: float, grad_scale: float, flag: Optional[torch.Tensor], stream=None,
                       loss_scaler: Optional[torch.Tensor] = None) -> None:
-    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _ptr(loss_scaler))
-    _check(lib().zero_adam_prepare(plan.handle, _ptr(live), _ptr(steps), ctypes.byref(hp), _ptr(flag),
-                                   _stream(stream)))
+    w = "zero_adam_prepare"
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _scaler(plan, loss_scaler, w))
+    _check(lib().zero_adam_prepare(plan.handle, _buf(plan, live, w + ": live", plan.n, U8),
+                                   _buf(plan, steps, w + ": steps", plan.n, I32), ctypes.byref(hp),
+                                   _buf(plan, flag, w + ": flag", 1, I32), _stream(stream)))
 
 
 def zero_reduce_adam_bucket(plan: Plan, b: int, rows: torch.Tensor, row_stride: int, live: torch.Tensor,
                             p32: torch.Tensor, m: torch.Tensor, v: torch.Tensor, flag: Optional[torch.Tensor],
                             arena: torch.Tensor, stream=None) -> None:
     """rows as in zero_reduce_shard; needs zero_adam_prepare earlier in the step on the same stream."""
-    _check(lib().zero_reduce_adam_bucket(plan.handle, b, _ptr(rows), row_stride, _ptr(live), _ptr(p32), _ptr(m),
-                                         _ptr(v), _ptr(flag), _ptr(arena), _stream(stream)))
+    S, w = plan.shard_numel, "zero_reduce_adam_bucket"
+    _check(lib().zero_reduce_adam_bucket(plan.handle, b, _buf(plan, rows, w + ": rows", plan.rows_elems(b, row_stride),
+                                                              elem_size=2),
+                                         row_stride, _buf(plan, live, w + ": live", plan.n, U8),
+                                         _buf(plan, p32, w + ": p32", S, F32), _buf(plan, m, w + ": m", S, F32),
+                                         _buf(plan, v, w + ": v", S, F32), _buf(plan, flag, w + ": flag", 1, I32),
+                                         _buf(plan, arena, w + ": arena", plan.arena_numel, elem_size=2),
+                                         _stream(stream)))
 
 
-LOSS_SCALER_BYTES = ctypes.sizeof(zero_loss_scaler)
 
 
 def zero_loss_scaler_init(cfg: zero_loss_scaler, scaler: torch.Tensor, stream=None) -> None:
@@ -283,6 +400,10 @@ def zero_loss_scaler_init(cfg: zero_loss_scaler, scaler: torch.Tensor, stream=No
 
 
 def zero_loss_scaler_update(flag: torch.Tensor, scaler: torch.Tensor, stream=None) -> None:
+    if flag is not None and (flag.numel() < 1 or flag.dtype != torch.int32):
+        raise ValueError("zero_loss_scaler_update: flag must be an int32 tensor of at least one element")
+    if scaler is not None and scaler.numel() * scaler.element_size() < LOSS_SCALER_BYTES:
+        raise ValueError("zero_loss_scaler_update: loss scaler tensor too small")
     _check(lib().zero_loss_scaler_update(_ptr(flag), _ptr(scaler), _stream(stream)))
 
 

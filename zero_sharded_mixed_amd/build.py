@@ -1,4 +1,5 @@
-"""Build libzero_shard.so (every HIP source under csrc/) for gfx950 with hipcc, in place."""
+"""Build libzero_shard.so (every HIP source under csrc/) and libzero_probe.so (the bandwidth
+probes under probe/) for gfx950 with hipcc, in place."""
 from __future__ import annotations
 
 import glob
@@ -9,6 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libzero_shard.so")
+PROBE_LIB = os.path.join(HERE, "libzero_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,18 +25,27 @@ def sources() -> list:
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), *sources(),
-           "-o", tmp]
+def probe_sources() -> list:
+    return sorted(glob.glob(os.path.join(HERE, "probe", "*.hip")))
+
+
+def _hipcc(srcs: list, out: str, verbose: bool) -> str:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"), *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libzero_shard.so")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both libraries (every call compiles); returns the pipeline library's path."""
+    _hipcc(probe_sources(), PROBE_LIB, verbose)
+    return _hipcc(sources(), LIB, verbose)
 
 
 if __name__ == "__main__":

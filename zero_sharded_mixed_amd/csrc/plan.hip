@@ -2,8 +2,9 @@
 // the row/shard placement and the tile maps the hot kernels search, all computed on the
 // device, then copied back so the host can answer info queries.
 //
-// Follows briefia.fr "L'IA sur plusieurs GPU : ZeRO et FSDP" (Implémentation simplifiée: the
-// remainder / pad / padded / shard_size / shard_start / shard_end formulas) and the ColossalAI
+// Follows briefia.fr "L'IA sur plusieurs GPU : ZeRO et FSDP" (Implémentation simplifiée: zero
+// padding to a multiple of the world size, the shard size, start and end of every rank's row)
+// and the ColossalAI
 // issue "[zero] improving compatibility of low level zero" (INIT: split every parameter evenly
 // over world_size; BWD: gradients gathered into buckets, flattened per rank).
 #include <stdarg.h>
@@ -74,17 +75,18 @@ struct PlanScratch {
 __global__ void plan_fields_kernel(PlanScratch T, const int64_t* __restrict__ numels, int64_t n, int64_t nd,
                                    int64_t rank) {
     for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) {
+        // Nd full rows: a row is the quotient of numel by Nd, one longer when a remainder
+        // is left; the zeros the rows hold beyond numel are the padding.
         const int64_t numel = numels[i];
-        const int64_t remainder = numel % nd;
-        const int64_t pad = (nd - remainder) % nd;
-        const int64_t padded = numel + pad;
-        const int64_t s = padded / nd;
+        const int64_t q = numel / nd;
+        const bool partial = q * nd != numel;
+        const int64_t s = partial ? q + 1 : q;
         T.numel[i] = numel;
-        T.pad[i] = pad;
-        T.padded[i] = padded;
         T.s[i] = s;
+        T.padded[i] = s * nd;
+        T.pad[i] = s * nd - numel;
         T.start[i] = rank * s;
-        T.sh_end[i] = rank * s + s;
+        T.sh_end[i] = (rank + 1) * s;
         T.uc[i] = (numel + kChunk - 1) / kChunk;
     }
 }

@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include "zero_shard.h"
+#include "zs_grid.h"
 
 namespace zs {
 
@@ -280,13 +281,4 @@ zero_status fail(zero_status st, const char* fmt, ...);
 zero_status check_launch(const char* what);
 zero_status check_device(const zero_plan* plan);
 inline bool host_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-// Hot kernels launch one block per work item (a tile, or a tile of one row): on MI355X a
-// one-shot grid with one 16-byte chunk per thread streams faster than a grid-stride loop.  The
-// kernels still loop, so any grid size is correct.
-#ifndef ZS_GRID_CAP
-#define ZS_GRID_CAP (int64_t(1) << 30)
-#endif
-inline int grid_for(int64_t work, int64_t cap = ZS_GRID_CAP) {
-    return int(work < 1 ? 1 : (work < cap ? work : cap));
-}
 }  // namespace zs

@@ -1,0 +1,111 @@
+// bandwidth.hip — memory-bandwidth probes in the pipeline kernels' access patterns (see
+// include/zero_probe.h).  Trivial arithmetic, the same launch shape as the pipeline: a one-shot
+// grid of 256-thread blocks, each thread one 16-byte chunk per stream, global (not flat)
+// 16-byte loads and stores.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_probe.h"
+
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int64_t kMaxBlocks = int64_t(1) << 23;  // fewer than 2^32 work-items per dispatch
+#define ZP_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld(const void* p) { return *(const ZP_GLOBAL u32x4*)p; }
+__device__ __forceinline__ void st(void* p, u32x4 v) { *(ZP_GLOBAL u32x4*)p = v; }
+__device__ __forceinline__ f32x4 ldf(const float* p) { return *(const ZP_GLOBAL f32x4*)p; }
+__device__ __forceinline__ void stf(float* p, f32x4 v) { *(ZP_GLOBAL f32x4*)p = v; }
+
+// chunks: 16-byte chunks of the stream; one per thread per iteration of the grid-stride loop
+__global__ __launch_bounds__(kBlock) void read_kernel(const u32x4* __restrict__ src, int64_t chunks,
+                                                      u32x4* __restrict__ sink) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t c = blockIdx.x * int64_t(kBlock) + threadIdx.x; c < chunks; c += int64_t(gridDim.x) * kBlock)
+        acc ^= ld(src + c);
+    if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u) st(sink, acc);
+}
+
+__global__ __launch_bounds__(kBlock) void write_kernel(u32x4* __restrict__ dst, int64_t chunks) {
+    for (int64_t c = blockIdx.x * int64_t(kBlock) + threadIdx.x; c < chunks; c += int64_t(gridDim.x) * kBlock) {
+        const uint32_t w = uint32_t(c);
+        const u32x4 v = {w, w ^ 0x55555555u, w ^ 0xaaaaaaaau, ~w};
+        st(dst + c, v);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                      int64_t chunks) {
+    for (int64_t c = blockIdx.x * int64_t(kBlock) + threadIdx.x; c < chunks; c += int64_t(gridDim.x) * kBlock)
+        st(dst + c, ld(src + c));
+}
+
+// groups: 8-column groups; thread = one group (two 16-byte accesses per fp32 stream)
+__global__ __launch_bounds__(kBlock) void adam_streams_kernel(const float* __restrict__ g, float* __restrict__ p,
+                                                              float* __restrict__ m, float* __restrict__ v,
+                                                              uint16_t* __restrict__ lp, int64_t groups) {
+    for (int64_t q = blockIdx.x * int64_t(kBlock) + threadIdx.x; q < groups; q += int64_t(gridDim.x) * kBlock) {
+        const int64_t x = 8 * q;
+        const f32x4 g0 = ldf(g + x), g1 = ldf(g + x + 4);
+        f32x4 p0 = ldf(p + x), p1 = ldf(p + x + 4);
+        f32x4 m0 = ldf(m + x), m1 = ldf(m + x + 4);
+        f32x4 v0 = ldf(v + x), v1 = ldf(v + x + 4);
+        p0 += g0, p1 += g1, m0 += g0, m1 += g1, v0 += g0, v1 += g1;
+        stf(p + x, p0), stf(p + x + 4, p1);
+        stf(m + x, m0), stf(m + x + 4, m1);
+        stf(v + x, v0), stf(v + x + 4, v1);
+        const u32x4 a = __builtin_bit_cast(u32x4, p0), b = __builtin_bit_cast(u32x4, p1);
+        const u32x4 h = {(a.x >> 16) | (a.y & 0xffff0000u), (a.z >> 16) | (a.w & 0xffff0000u),
+                         (b.x >> 16) | (b.y & 0xffff0000u), (b.z >> 16) | (b.w & 0xffff0000u)};
+        st(lp + x, h);
+    }
+}
+
+int grid(int64_t threads) {
+    const int64_t blocks = (threads + kBlock - 1) / kBlock;
+    return int(blocks < 1 ? 1 : blocks < kMaxBlocks ? blocks : kMaxBlocks);
+}
+
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+zero_status launched() { return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO_EHIP; }
+
+}  // namespace
+
+extern "C" zero_status zero_probe_read(const void* d_src, int64_t bytes, void* d_sink, void* stream) {
+    if (!d_src || !d_sink || bytes <= 0 || bytes % 16 || !a16(d_src) || !a16(d_sink)) return ZERO_EINVAL;
+    const int64_t chunks = bytes / 16;
+    read_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(d_src), chunks,
+                                                                  static_cast<u32x4*>(d_sink));
+    return launched();
+}
+
+extern "C" zero_status zero_probe_write(void* d_dst, int64_t bytes, void* stream) {
+    if (!d_dst || bytes <= 0 || bytes % 16 || !a16(d_dst)) return ZERO_EINVAL;
+    const int64_t chunks = bytes / 16;
+    write_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<u32x4*>(d_dst), chunks);
+    return launched();
+}
+
+extern "C" zero_status zero_probe_copy(const void* d_src, void* d_dst, int64_t bytes, void* stream) {
+    if (!d_src || !d_dst || bytes <= 0 || bytes % 16 || !a16(d_src) || !a16(d_dst)) return ZERO_EINVAL;
+    const char* s = static_cast<const char*>(d_src);
+    const char* d = static_cast<const char*>(d_dst);
+    if (s < d + bytes && d < s + bytes) return ZERO_EINVAL;  // overlapping buffers
+    const int64_t chunks = bytes / 16;
+    copy_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(d_src),
+                                                                  static_cast<u32x4*>(d_dst), chunks);
+    return launched();
+}
+
+extern "C" zero_status zero_probe_adam_streams(const float* d_g, float* d_p, float* d_m, float* d_v, uint16_t* d_lp,
+                                               int64_t n, void* stream) {
+    if (!d_g || !d_p || !d_m || !d_v || !d_lp || n <= 0 || n % 8) return ZERO_EINVAL;
+    if (!a16(d_g) || !a16(d_p) || !a16(d_m) || !a16(d_v) || !a16(d_lp)) return ZERO_EINVAL;
+    const int64_t groups = n / 8;
+    adam_streams_kernel<<<grid(groups), kBlock, 0, (hipStream_t)stream>>>(d_g, d_p, d_m, d_v, d_lp, groups);
+    return launched();
+}

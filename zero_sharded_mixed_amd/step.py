@@ -59,13 +59,20 @@ class ShardStep:
 
     # -- views ---------------------------------------------------------------------------
     def block(self, buf: torch.Tensor, b: int) -> torch.Tensor:
+        """Bucket b's [Nd][L_b] block of an arena-layout buffer (ValueError if buf is shorter
+        than the arena)."""
         bk = self.buckets[b]
-        return buf[bk.block_offset:bk.block_offset + self.nd * bk.row_stride]
+        end = bk.block_offset + self.nd * bk.row_stride
+        if buf.numel() < end:
+            raise ValueError(f"buffer of {buf.numel()} elements is shorter than bucket {b}'s block end {end}")
+        return buf[bk.block_offset:end]
 
     def own_row(self, buf: torch.Tensor, b: int, k: Optional[int] = None) -> torch.Tensor:
         bk = self.buckets[b]
         k = self.rank if k is None else k
         start = bk.block_offset + k * bk.row_stride
+        if not 0 <= k < self.nd or buf.numel() < start + bk.row_stride:
+            raise ValueError(f"row {k} of bucket {b} does not fit a buffer of {buf.numel()} elements")
         return buf[start:start + bk.row_stride]
 
     # -- the steps -----------------------------------------------------------------------
