@@ -304,6 +304,27 @@ zero_status zero_unpack(const zero_plan* plan, int64_t b, const void* d_gathered
 zero_status zero_shard_init(const zero_plan* plan, const void* const* d_src_ptrs, int32_t src_dtype, float* d_p32,
                             void* stream);
 
+/* ------------------------------------------------- allocation-free Adam step ------ */
+
+/* Largest plan (in parameters) that zero_adam_step_noalloc serves. */
+#define ZERO_ADAM_NOALLOC_MAX_PARAMS 131072
+
+/* zero_adam_step for callers that cannot allocate device memory or use the plan's scratch
+ * (code under graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and the same results, bit for bit, but the per-parameter step sizes and the
+ * fp32 hyperparameters are staged in a static device array of 1 MiB + 256 bytes
+ * (ZERO_ADAM_NOALLOC_MAX_PARAMS * 8 + 256) that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates nothing and calls no allocating routine; its
+ * first use on a device looks up the array's address there (hipGetSymbolAddress).  Every
+ * call on one GPU shares that GPU's array, which keeps the last call's contents (every value
+ * a step reads is written earlier in the same step): calls that overlap in time on one GPU
+ * -- on different streams, or from different plans -- race and must not be issued.
+ * Arguments and errors as zero_adam_step, plus ZERO_ERANGE when the plan has more than
+ * ZERO_ADAM_NOALLOC_MAX_PARAMS parameters (nothing is launched). */
+zero_status zero_adam_step_noalloc(const zero_plan* plan, const float* d_g32, float* d_p32, float* d_m, float* d_v,
+                                   const uint8_t* d_live, int32_t* d_steps, const zero_adam_hparams* hp,
+                                   const int32_t* d_flag, void* d_arena, void* stream);
+
 /* ------------------------------------------- fused path: reduce + check + Adam ------ */
 /* The same step with the reduced gradient kept in registers: the sum of the Nd rows goes
  * straight into the Adam update, so the fp32 gradient shard is neither written nor read.

@@ -6,7 +6,7 @@ torch device tensors.  PyTorch provides device memory and streams only.
 """
 from ._binding import (EXPORTS, LIB_PATH, LOSS_SCALER_BYTES, ZERO_BF16, ZERO_EHIP, ZERO_EINVAL, ZERO_ENOMEM,
                        ZERO_ERANGE, ZERO_FP16, ZERO_OK, Plan, ZeroError, lib, ptr_table, read_loss_scaler,
-                       zero_adam_prepare, zero_adam_step, zero_bucket_info, zero_last_error, zero_loss_scaler,
+                       zero_adam_prepare, zero_adam_step, zero_adam_step_noalloc, zero_bucket_info, zero_last_error, zero_loss_scaler,
                        zero_loss_scaler_init, zero_loss_scaler_update, zero_model_state_bytes, zero_overflow_check,
                        zero_pack_bucket, zero_pack_bucket_check, zero_param_info, zero_plan_bucket_info,
                        zero_plan_create, zero_plan_create_grouped, zero_plan_destroy, zero_plan_get_summary,
@@ -15,7 +15,7 @@ from ._binding import (EXPORTS, LIB_PATH, LOSS_SCALER_BYTES, ZERO_BF16, ZERO_EHI
 from .step import ShardStep, Zero3Schedule
 
 __all__ = ["EXPORTS", "LIB_PATH", "LOSS_SCALER_BYTES", "Plan", "ShardStep", "Zero3Schedule", "ZeroError", "lib",
-           "ptr_table", "read_loss_scaler", "zero_adam_prepare", "zero_adam_step", "zero_bucket_info",
+           "ptr_table", "read_loss_scaler", "zero_adam_prepare", "zero_adam_step", "zero_adam_step_noalloc", "zero_bucket_info",
            "zero_last_error",
            "zero_loss_scaler", "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_model_state_bytes",
            "zero_overflow_check", "zero_pack_bucket", "zero_pack_bucket_check", "zero_param_info",

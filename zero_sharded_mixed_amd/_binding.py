@@ -26,7 +26,8 @@ EXPORTS = ("zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy", 
            "zero_plan_param_info", "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes",
            "zero_pack_bucket", "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack",
            "zero_shard_init", "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket",
-           "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_last_error")
+           "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_last_error", "zero_adam_step_noalloc")
+ADAM_NOALLOC_MAX_PARAMS = 131072  # ZERO_ADAM_NOALLOC_MAX_PARAMS
 
 
 class ZeroError(RuntimeError):
@@ -97,6 +98,7 @@ def lib() -> ctypes.CDLL:
         "zero_reduce_shard": (i32, [vp, i64, vp, i64, vp, vp, vp, vp]),
         "zero_overflow_check": (i32, [vp, vp, vp, vp, vp]),
         "zero_adam_step": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
+        "zero_adam_step_noalloc": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
         "zero_unpack": (i32, [vp, i64, vp, vp, vp]),
         "zero_shard_init": (i32, [vp, vp, i32, vp, vp]),
         "zero_pack_bucket_check": (i32, [vp, i64, vp, vp, vp, vp]),
@@ -344,6 +346,22 @@ def zero_adam_step(plan: Plan, g32: torch.Tensor, p32: torch.Tensor, m: torch.Te
                                 _buf(plan, live, w + ": live", plan.n, U8), _buf(plan, steps, w + ": steps", plan.n, I32),
                                 ctypes.byref(hp), _buf(plan, flag, w + ": flag", 1, I32),
                                 _buf(plan, arena, w + ": arena", plan.arena_numel, elem_size=2), _stream(stream)))
+
+
+def zero_adam_step_noalloc(plan: Plan, g32: torch.Tensor, p32: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                           live: torch.Tensor, steps: torch.Tensor, lr: float, beta1: float, beta2: float,
+                           eps: float, grad_scale: float, flag: Optional[torch.Tensor], arena: torch.Tensor,
+                           stream=None, loss_scaler: Optional[torch.Tensor] = None) -> None:
+    """zero_adam_step with its staging in the library's static device array (no allocation)."""
+    S, w = plan.shard_numel, "zero_adam_step_noalloc"
+    hp = zero_adam_hparams(lr, beta1, beta2, eps, grad_scale, _scaler(plan, loss_scaler, w))
+    _check(lib().zero_adam_step_noalloc(plan.handle, _buf(plan, g32, w + ": g32", S, F32),
+                                        _buf(plan, p32, w + ": p32", S, F32), _buf(plan, m, w + ": m", S, F32),
+                                        _buf(plan, v, w + ": v", S, F32), _buf(plan, live, w + ": live", plan.n, U8),
+                                        _buf(plan, steps, w + ": steps", plan.n, I32), ctypes.byref(hp),
+                                        _buf(plan, flag, w + ": flag", 1, I32),
+                                        _buf(plan, arena, w + ": arena", plan.arena_numel, elem_size=2),
+                                        _stream(stream)))
 
 
 def zero_unpack(plan: Plan, b: int, gathered: torch.Tensor, param_ptrs: torch.Tensor, stream=None) -> None:

@@ -18,6 +18,7 @@
 // and writing p32, m, v and the 16-bit parameters — 30 bytes per element.
 // Both kernels return at once when the flag is set, so a skipped step changes nothing.
 #include <cmath>
+#include <mutex>
 
 #include "zs_adam.h"
 
@@ -165,8 +166,11 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int
 using namespace zs;
 
 namespace zs {
-zero_status launch_adam_prepare(const zero_plan* plan, const uint8_t* d_live, int32_t* d_steps,
-                                const zero_adam_hparams* hp, const int32_t* d_flag, hipStream_t s, const char* who) {
+// The prepare kernel writes every live parameter's step sizes into scal[n] and the fp32
+// hyperparameters into consts[kAdamConsts]: the plan's scratch, or the static array below.
+zero_status launch_adam_prepare_to(const zero_plan* plan, const uint8_t* d_live, int32_t* d_steps,
+                                   const zero_adam_hparams* hp, const int32_t* d_flag, float2* scal, float* consts,
+                                   hipStream_t s, const char* who) {
     if (!d_live || !d_steps || !hp) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
     if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps) || !std::isfinite(hp->grad_scale) || !(hp->beta1 >= 0.0) ||
         !(hp->beta1 < 1.0) || !(hp->beta2 >= 0.0) || !(hp->beta2 < 1.0))
@@ -175,7 +179,40 @@ zero_status launch_adam_prepare(const zero_plan* plan, const uint8_t* d_live, in
         return fail(ZERO_EINVAL, "%s: loss scaler not 4-byte aligned", who);
     adam_prepare_kernel<<<grid_for((plan->n + 255) / 256, 1024), 256, 0, s>>>(
         plan->dev, d_live, d_steps, d_flag, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->grad_scale, hp->loss_scaler,
-        reinterpret_cast<float2*>(plan->d_adam_scal), plan->d_adam_const);
+        scal, consts);
+    return check_launch(who);
+}
+
+zero_status launch_adam_prepare(const zero_plan* plan, const uint8_t* d_live, int32_t* d_steps,
+                                const zero_adam_hparams* hp, const int32_t* d_flag, hipStream_t s, const char* who) {
+    return launch_adam_prepare_to(plan, d_live, d_steps, hp, d_flag, reinterpret_cast<float2*>(plan->d_adam_scal),
+                                  plan->d_adam_const, s, who);
+}
+
+// Argument checks, then the prepare kernel and the streaming kernel, with the step sizes
+// staged in scal / consts.
+static zero_status adam_step_with(const zero_plan* plan, const float* d_g32, float* d_p32, float* d_m, float* d_v,
+                                  const uint8_t* d_live, int32_t* d_steps, const zero_adam_hparams* hp,
+                                  const int32_t* d_flag, void* d_arena, float2* scal, float* consts, void* stream,
+                                  const char* who) {
+    // an empty shard still advances the step counts of live parameters; its arrays may be NULL
+    if (plan->shard_numel != 0 && (!d_g32 || !d_p32 || !d_m || !d_v || !d_arena))
+        return fail(ZERO_EINVAL, "%s: NULL pointer", who);
+    if (!host_aligned16(d_g32) || !host_aligned16(d_p32) || !host_aligned16(d_m) || !host_aligned16(d_v) ||
+        !host_aligned16(d_arena))
+        return fail(ZERO_EINVAL, "%s: shard arrays and arena must be 16-byte aligned", who);
+    hipStream_t s = (hipStream_t)stream;
+    zero_status st = launch_adam_prepare_to(plan, d_live, d_steps, hp, d_flag, scal, consts, s, who);
+    if (st != ZERO_OK) return st;
+    if (plan->shard_numel == 0) return ZERO_OK;
+    AdamArgs A{d_g32, d_p32, d_m, d_v, d_live, scal, consts, d_flag, static_cast<uint16_t*>(d_arena)};
+    const int64_t span = int64_t(kBlock) * kAdamCols;
+    const int64_t n_spans = (plan->shard_numel + span - 1) / span;
+    const int g = grid_for(n_spans);
+    if (plan->dtype == ZERO_BF16)
+        adam_kernel<ZERO_BF16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
+    else
+        adam_kernel<ZERO_FP16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
     return check_launch(who);
 }
 }  // namespace zs
@@ -192,23 +229,55 @@ extern "C" zero_status zero_adam_step(const zero_plan* plan, const float* d_g32,
                                       const int32_t* d_flag, void* d_arena, void* stream) {
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
-    // an empty shard still advances the step counts of live parameters; its arrays may be NULL
-    if (plan->shard_numel != 0 && (!d_g32 || !d_p32 || !d_m || !d_v || !d_arena))
-        return fail(ZERO_EINVAL, "zero_adam_step: NULL pointer");
-    if (!host_aligned16(d_g32) || !host_aligned16(d_p32) || !host_aligned16(d_m) || !host_aligned16(d_v) ||
-        !host_aligned16(d_arena))
-        return fail(ZERO_EINVAL, "zero_adam_step: shard arrays and arena must be 16-byte aligned");
-    hipStream_t s = (hipStream_t)stream;
-    float2* scal = reinterpret_cast<float2*>(plan->d_adam_scal);
-    if ((st = launch_adam_prepare(plan, d_live, d_steps, hp, d_flag, s, "zero_adam_step")) != ZERO_OK) return st;
-    if (plan->shard_numel == 0) return ZERO_OK;
-    AdamArgs A{d_g32, d_p32, d_m, d_v, d_live, scal, plan->d_adam_const, d_flag, static_cast<uint16_t*>(d_arena)};
-    const int64_t span = int64_t(kBlock) * kAdamCols;
-    const int64_t n_spans = (plan->shard_numel + span - 1) / span;
-    const int g = grid_for(n_spans);
-    if (plan->dtype == ZERO_BF16)
-        adam_kernel<ZERO_BF16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
-    else
-        adam_kernel<ZERO_FP16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
-    return check_launch("zero_adam_step");
+    return adam_step_with(plan, d_g32, d_p32, d_m, d_v, d_live, d_steps, hp, d_flag, d_arena,
+                          reinterpret_cast<float2*>(plan->d_adam_scal), plan->d_adam_const, stream, "zero_adam_step");
+}
+
+// ------------------------------------------------------------- allocation-free variant --
+// zero_adam_step with the step-size staging in a file-scope device array instead of the
+// plan's scratch, for callers that cannot allocate.  One copy of the array per GPU, shared
+// by every call on that GPU and kept until the process ends; its device address is looked up
+// once per device (hipGetSymbolAddress) and only that address is passed to kernels.
+constexpr int64_t kNoAllocMaxParams = ZERO_ADAM_NOALLOC_MAX_PARAMS;
+constexpr size_t kNoAllocConstsOffset = size_t(kNoAllocMaxParams) * sizeof(float2);
+constexpr size_t kNoAllocBytes = kNoAllocConstsOffset + 256;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up once per device).
+zero_status scratch_on_device(int dev, void** out, const char* who) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZERO_EINVAL, "%s: device %d beyond %d", who, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(ZERO_EHIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZERO_OK;
+}
+}  // namespace
+
+extern "C" zero_status zero_adam_step_noalloc(const zero_plan* plan, const float* d_g32, float* d_p32, float* d_m,
+                                              float* d_v, const uint8_t* d_live, int32_t* d_steps,
+                                              const zero_adam_hparams* hp, const int32_t* d_flag, void* d_arena,
+                                              void* stream) {
+    const char* who = "zero_adam_step_noalloc";
+    zero_status st = check_device(plan);
+    if (st != ZERO_OK) return st;
+    if (plan->n > kNoAllocMaxParams)
+        return fail(ZERO_ERANGE, "%s: %lld parameters exceed the static scratch's maximum of %lld", who,
+                    (long long)plan->n, (long long)kNoAllocMaxParams);
+    void* base = nullptr;
+    if ((st = scratch_on_device(plan->device, &base, who)) != ZERO_OK) return st;
+    float2* scal = static_cast<float2*>(base);
+    float* consts = reinterpret_cast<float*>(static_cast<char*>(base) + kNoAllocConstsOffset);
+    return adam_step_with(plan, d_g32, d_p32, d_m, d_v, d_live, d_steps, hp, d_flag, d_arena, scal, consts, stream,
+                          who);
 }
