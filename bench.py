@@ -722,8 +722,9 @@ def summarize_profiles(root: str, workload: str, command: str, pid: str = "") ->
         lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
+    extra = extra_counters(root, pid)
     if not glob.glob(os.path.join(root, "FETCH_SIZE")):  # a kernel trace alone: no traffic section
-        return "\n".join(lines) + "\n"
+        return "\n".join(lines + extra) + "\n"
     traffic = {}
     counters = {}
     for cname in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -760,6 +761,7 @@ def summarize_profiles(root: str, workload: str, command: str, pid: str = "") ->
         traffic[short] = {"bytes_per_launch": int(b), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                           "dispatches": len(vals), "source_hash": src_hash}
         lines.append(f"| {short} | {len(vals)} | {fk:.0f} | {wk:.0f} | {b:.3e} |")
+    lines += extra
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -770,6 +772,41 @@ def summarize_profiles(root: str, workload: str, command: str, pid: str = "") ->
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(allt, fh, indent=1, sort_keys=True)
     return "\n".join(lines) + "\n"
+
+
+def extra_counters(root: str, pid: str = "") -> list:
+    """Lines of a table per further --pmc pass under root (every directory other than trace/,
+    FETCH_SIZE/ and WRITE_SIZE/): the average per dispatch of each counter, per kernel."""
+    import csv
+    import glob
+
+    out = []
+    for d in sorted(os.listdir(root)) if os.path.isdir(root) else []:
+        if d in ("trace", "FETCH_SIZE", "WRITE_SIZE") or not os.path.isdir(os.path.join(root, d)):
+            continue
+        files = sorted(glob.glob(os.path.join(root, d, "**", "*counter_collection.csv"), recursive=True))
+        if pid:
+            files = [f for f in files if os.path.basename(f).startswith(f"{pid}_")]
+        if not files:
+            continue
+        per = {}
+        with open(files[0]) as fh:
+            for r in csv.DictReader(fh):
+                short = _short(r["Kernel_Name"])
+                if short not in SHORT_NAMES:
+                    continue
+                per.setdefault(short, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        names = sorted({c for v in per.values() for c in v})
+        if not names:
+            continue
+        out += ["", f"## Counters, pass `{d}` (--pmc; average per dispatch)", "",
+                "| kernel | dispatches | " + " | ".join(names) + " |", "|---" * (len(names) + 2) + "|"]
+        for k in sorted(per):
+            vals = per[k]
+            nd = max(len(v) for v in vals.values())
+            out.append(f"| {k} | {nd} | " + " | ".join(
+                f"{sum(vals[c]) / len(vals[c]):.4g}" if c in vals else "" for c in names) + " |")
+    return out
 
 
 # -------------------------------------------------------------------------------- main --

@@ -9,12 +9,12 @@
 //
 // Work decomposition.  Both the pack and the shard init are driven by their OUTPUT, one
 // 16-byte chunk (8 elements of a 16-bit block, or 8 fp32 shard columns) per thread: every
-// store is an aligned dwordx4 (rows start 16-byte aligned because L_b is a multiple of 8), and
-// the parameter that owns a chunk is found through the shard tile map.  A chunk that lies
-// inside one parameter reads its 8 source elements with at most two aligned 16-byte loads
-// and a funnel shift (load8_realigned); chunks that straddle parameters, padding or a row gap
-// fall back to per-element work.  The unpack is driven by its output too, in per-parameter
-// chunk space.
+// store is an aligned dwordx4 (rows start 16-byte aligned because L_b is a multiple of 8).  A
+// chunk that lies inside one parameter reads its 8 source elements with one 16-byte load at
+// whatever alignment the row has in the gradient (k * s_i + column); chunks that straddle
+// parameters, padding or a row gap go element by element.  The pack's blocks follow per-bucket
+// lists of whole and mixed tiles built with the plan (see pack_kernel).  The unpack is driven
+// by its output too, in per-parameter chunk space.
 #include <cmath>
 #include <cstring>
 
@@ -23,13 +23,9 @@
 namespace zs {
 
 // ------------------------------------------------------------------------------- pack --
-#ifndef ZS_PACK_ROWS
-#define ZS_PACK_ROWS 2
-#endif
 #ifndef ZS_UNPACK_UNROLL
 #define ZS_UNPACK_UNROLL 2
 #endif
-constexpr int kPackRows = ZS_PACK_ROWS;          // rows per block iteration of the pack
 constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
 
 // The input check of the checked pack: true if one of the eight 16-bit values is inf or NaN
@@ -46,6 +42,18 @@ __device__ __forceinline__ bool out_of_range8(const uint4& v, uint32_t limit) {
     return bad;
 }
 
+// Eight elements of one row of parameter m, starting at element e of its flat gradient:
+// one unaligned 16-byte load when all eight are gradient elements, else element by element
+// with +0 for the padding (e >= numel).
+__device__ __forceinline__ uint4 row_chunk(const uint16_t* g, int64_t e, int64_t numel) {
+    if (e + kChunk <= numel) return load16_any(g + e);
+    const ZS_GLOBAL uint16_t* gg = gptr(g);
+    uint16_t h[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[t] = (e + t < numel) ? gg[e + t] : uint16_t(0);
+    return pack8(h);
+}
+
 // Generic per-thread pack of one 8-column chunk of row k (parameter boundaries, padding,
 // row gaps, dead parameters, unaligned sources).  i is the first parameter with end > x.
 template <bool CHECK>
@@ -55,18 +63,7 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
     if (i < P.n && P.off[i] <= x && x + kChunk <= P.end[i]) {
         const uint16_t* g = grads[i];
         if (!g) return;  // no gradient this step: leave the slots alone
-        const int64_t numel = P.numel[i];
-        const int64_t e0 = k * P.s[i] + (x - P.off[i]);
-        uint4 v;
-        if (e0 + kChunk <= numel && aligned16(g)) {
-            v = load8_realigned(g, e0);
-        } else {
-            const ZS_GLOBAL uint16_t* gg = gptr(g);
-            uint16_t h[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
-            v = pack8(h);
-        }
+        const uint4 v = row_chunk(g, k * P.s[i] + (x - P.off[i]), P.numel[i]);
         if constexpr (CHECK) bad |= out_of_range8(v, limit);
         store16(dst, v);
         return;
@@ -97,159 +94,215 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
     }
 }
 
-// Tiles holding several parameters: the block stages the fields of every parameter that
-// overlaps the tile in LDS once, and each thread finds its chunk's parameter there (a binary
-// search in LDS instead of dependent global loads).  Tiles touching more than kStageMax
-// parameters use the unstaged generic path.
+// Mixed tiles stage the parameters that overlap them in LDS (at most kStageMax; tiles touching
+// more parameters go chunk by chunk through the generic path).
 #ifndef ZS_STAGE_MAX
 #define ZS_STAGE_MAX 256
 #endif
 constexpr int kStageMax = ZS_STAGE_MAX;
-struct PackMeta {
-    int64_t off, end, s, numel;
+
+// Work items of one bucket, in dispatch order:
+//  * mixed tiles (several parameters, padding, the row gap): kMixRows rows of one tile per
+//    block, tiles varying fastest, by runs (above); they come first, so that these heavier
+//    blocks do not form the launch's tail;
+//  * whole tiles (a tile inside one parameter): kWholeRows rows of one tile per block, rows
+//    varying fastest.  Each block moves only kWholeRows * 4 KB behind a chain of dependent loads
+//    (list entry -> parameter fields and gradient pointer -> data), so the chain is kept at that
+//    length (the list entry carries the parameter) and the rows of a block share it.
+// Measured on MI355X: one row per block, four, or tiles varying fastest, lose 2-20% on the
+// whole-tile lists; a fixed grid that prefetches the next item loses 10-40% against this
+// one-block-per-item grid; 4, 16 or 32 rows per mixed block are slower than 8.
+// tiles: the bucket's n_whole whole tiles, then its n_mixed mixed tiles (plan tables).
+#ifndef ZS_MIX_ROWS
+#define ZS_MIX_ROWS 8
+#endif
+#ifndef ZS_WHOLE_ROWS
+#define ZS_WHOLE_ROWS 2
+#endif
+constexpr int kMixRows = ZS_MIX_ROWS;        // rows per block of a mixed tile
+constexpr int kWholeRows = ZS_WHOLE_ROWS;    // rows per block of a whole tile
+
+// The fields a whole-tile work item needs: its rows, its columns' parameter and that
+// parameter's gradient pointer (NULL = no gradient this step).
+struct WholeItem {
+    int64_t k0, x0, off, s, numel;
     const uint16_t* g;
 };
 
-// First staged index t in [0, cnt] with sm[t].end > x.
-__device__ __forceinline__ int staged_search(const PackMeta* sm, int cnt, int64_t x) {
-    int lo = 0, hi = cnt;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sm[mid].end > x) hi = mid; else lo = mid + 1;
-    }
-    return lo;
+__device__ __forceinline__ WholeItem whole_item(const DevPlan& P, const int64_t* __restrict__ tiles,
+                                                const uint16_t* const* __restrict__ grads, int64_t w, int64_t n_wrg,
+                                                int64_t n_whole) {
+    // rows vary fastest: consecutive blocks take the row groups of one tile
+    const int64_t jw = n_whole * n_wrg <= int64_t(UINT32_MAX) ? int64_t(uint32_t(w) / uint32_t(n_wrg)) : w / n_wrg;
+    const int64_t rg = w - jw * n_wrg;
+    const int64_t j = ld_const(tiles, 2 * jw), i = ld_const(tiles, 2 * jw + 1);  // the tile, its parameter
+    return WholeItem{rg * kWholeRows, j << kTileShift, ld_const(P.off, i), ld_const(P.s, i), ld_const(P.numel, i),
+                     ld_const(grads, i)};
 }
 
 template <bool CHECK>
-__device__ __forceinline__ void pack_chunk_staged(const PackMeta* sm, int cnt, int t0, int64_t k, int64_t x,
-                                                  uint16_t* dst, uint32_t limit, bool& bad) {
-    if (t0 < cnt && sm[t0].off <= x && x + kChunk <= sm[t0].end) {
-        const PackMeta& m = sm[t0];
-        if (!m.g) return;  // no gradient this step
-        const int64_t e0 = k * m.s + (x - m.off);
-        uint4 v;
-        if (e0 + kChunk <= m.numel && aligned16(m.g)) {
-            v = load8_realigned(m.g, e0);
+__device__ __forceinline__ void whole_loads(const DevPlan& P, const WholeItem& it, uint4 (&v)[kWholeRows],
+                                            uint32_t limit, bool& bad) {
+    const int64_t c = it.x0 + int64_t(threadIdx.x) * kChunk - it.off;
+#pragma unroll
+    for (int u = 0; u < kWholeRows; ++u) {
+        if (it.k0 + u >= P.nd) break;
+        v[u] = row_chunk(it.g, (it.k0 + u) * it.s + c, it.numel);
+        if constexpr (CHECK) bad |= out_of_range8(v[u], limit);
+    }
+}
+
+__device__ __forceinline__ void whole_stores(const DevPlan& P, const WholeItem& it, const uint4 (&v)[kWholeRows],
+                                             uint16_t* __restrict__ packed, int64_t b_base, int64_t b_stride) {
+    uint16_t* dst = packed + (it.x0 + int64_t(threadIdx.x) * kChunk - b_base);
+#pragma unroll
+    for (int u = 0; u < kWholeRows; ++u) {
+        if (it.k0 + u >= P.nd) break;
+        store16(dst + (it.k0 + u) * b_stride, v[u]);
+    }
+}
+
+// Mixed tiles, by runs.  Row k of a bucket is the concatenation of the parameters' row
+// pieces, piece i being elements [k * s_i, (k + 1) * s_i) of gradient i.  A piece of s_i >= 8
+// columns is cut into runs of 8 starting at the parameter's first column, the last run moved
+// back to end exactly at the piece's end (it overlaps its predecessor, which writes the same
+// values); each run of each row is then one 16-byte load from the gradient and one 16-byte
+// store into the row, both at whatever alignment they have.  A mixed tile takes every run that
+// intersects it: a run crossing into a whole tile rewrites that tile's values there, and a run
+// crossing two mixed tiles is written by both, always with the same values.  Pieces shorter
+// than 8 columns, runs that reach into the padding (their elements at or past numel_i are +0)
+// and the row gap [S_b, L_b) (+0) go element by element.  A parameter without a gradient has
+// no runs: its columns are not written.
+struct MixMeta {
+    int64_t off, s, numel;
+    const uint16_t* g;
+    int64_t mlo;    // the parameter's first run that intersects the tile
+    int32_t run0;   // index of that run in the tile's list (exclusive scan of the run counts)
+};
+
+template <bool CHECK>
+__device__ __forceinline__ void pack_run(const MixMeta& m, int64_t mnum, int64_t k0, int64_t k1,
+                                         uint16_t* __restrict__ packed, int64_t b_base, int64_t b_stride,
+                                         uint32_t limit, bool& bad) {
+    const int64_t s = m.s;
+    const int64_t j = (s >= kChunk && 8 * mnum + kChunk > s) ? s - kChunk : 8 * mnum;  // first element of the run
+    const int len = int(s - j < kChunk ? s - j : kChunk);
+    const uint16_t* src = m.g + j;
+    const int64_t lim = m.numel - j;  // element e of the run exists iff k * s + e < lim
+    uint16_t* dst = packed + (m.off + j - b_base);
+    for (int64_t k = k0; k < k1; ++k) {
+        const int64_t e = k * s;
+        if (len == kChunk && e + kChunk <= lim) {
+            const uint4 v = load16_any(src + e);
+            if constexpr (CHECK) bad |= out_of_range8(v, limit);
+            store16_any(dst + k * b_stride, v);
         } else {
-            const ZS_GLOBAL uint16_t* gg = gptr(m.g);
+            ZS_GLOBAL uint16_t* d = gptr(dst + k * b_stride);
             uint16_t h[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) h[t] = (e0 + t < m.numel) ? gg[e0 + t] : uint16_t(0);
-            v = pack8(h);
+            for (int t = 0; t < 8; ++t) {
+                h[t] = (t < len && e + t < lim) ? gptr(src)[e + t] : uint16_t(0);
+                if (t < len) d[t] = h[t];
+            }
+            if constexpr (CHECK) bad |= out_of_range8(pack8(h), limit);
         }
-        if constexpr (CHECK) bad |= out_of_range8(v, limit);
-        store16(dst, v);
-        return;
-    }
-    uint16_t h[8];
-    unsigned keep = 0;
-    int i = t0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int64_t xt = x + t;
-        while (i < cnt && sm[i].end <= xt) ++i;
-        h[t] = 0;
-        if (i < cnt && sm[i].off <= xt) {
-            const uint16_t* g = sm[i].g;
-            if (!g) continue;
-            const int64_t e = k * sm[i].s + (xt - sm[i].off);
-            if (e < sm[i].numel) h[t] = gptr(g)[e];
-        }
-        keep |= 1u << t;
-    }
-    if constexpr (CHECK) bad |= out_of_range8(pack8(h), limit);
-    if (keep == 0xffu) {
-        store16(dst, pack8(h));
-    } else {
-        ZS_GLOBAL uint16_t* d = gptr(dst);
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            if (keep & (1u << t)) d[t] = h[t];
     }
 }
 
-// Work item w = (tile, group of kPackRows rows) of the bucket, rows varying fastest (on MI355X
-// this dispatch order streams faster than tile-fastest).  When the whole tile lies inside one
-// parameter with a 16-byte aligned gradient (decided once per block from scalar loads), each
-// thread issues the loads of its rows before any store.
-// CHECK: also OR 1 into *flag when a gradient element is non-finite or above `limit`.
+// One mixed-tile work item: rows [kg * kMixRows, ...) of mixed tile jm.  The parameters that
+// overlap the tile are staged with their run counts; each thread takes runs r = tid, tid + 256, ...
 template <bool CHECK>
-__global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_stride, int64_t tile0,
-                                                      int64_t n_tile, int64_t n_rg,
-                                                      const uint16_t* const* __restrict__ grads,
+__device__ __forceinline__ void pack_mixed_item(const DevPlan& P, MixMeta* sm, int32_t* s_total, int64_t b_base,
+                                                int64_t b_row, int64_t b_stride, const int64_t* __restrict__ tiles,
+                                                int64_t jm, int64_t kg, const uint16_t* const* __restrict__ grads,
+                                                uint16_t* __restrict__ packed, uint32_t limit, bool& bad) {
+    const int64_t j = ld_const(tiles, 2 * jm);
+    const int64_t x0 = j << kTileShift, x1 = x0 + kTileCols;
+    const int64_t k0 = kg * kMixRows, k1 = k0 + kMixRows < P.nd ? k0 + kMixRows : P.nd;
+    // parameters overlapping the tile: [iu, last], last = the tile map's next entry (clamped)
+    const int64_t iu = ld_const(tiles, 2 * jm + 1);
+    const int64_t inext = ld_const(P.tile_first, j + 1);
+    const int64_t last = inext < P.n ? inext : P.n - 1;
+    const int64_t cnt = iu < P.n ? last - iu + 1 : 0;
+    // the row gap of this bucket, where it falls in the tile: +0 in every row
+    const int64_t gap0 = b_base + b_row, gap1 = b_base + b_stride;
+    if (gap0 < gap1 && gap0 < x1 && gap1 > x0 && threadIdx.x == 0) {
+        const int64_t c0 = gap0 > x0 ? gap0 : x0, c1 = gap1 < x1 ? gap1 : x1;
+        for (int64_t k = k0; k < k1; ++k)
+            for (int64_t c = c0; c < c1; ++c) gptr(packed)[k * b_stride + (c - b_base)] = 0;
+    }
+    if (cnt > kStageMax) {  // more parameters than the stage holds: chunk by chunk, unstaged
+        const int64_t x = x0 + int64_t(threadIdx.x) * kChunk;
+        if (x < b_base || x >= b_base + b_stride) return;
+        const int64_t i = param_of_column(P, x);
+        for (int64_t k = k0; k < k1; ++k)
+            pack_chunk_generic<CHECK>(P, i, k, x, grads, packed + k * b_stride + (x - b_base), limit, bad);
+        return;
+    }
+    __syncthreads();  // the previous item's readers are done with the stage
+    for (int64_t t = threadIdx.x; t < cnt; t += kBlock) {
+        const int64_t pi = iu + t;
+        const int64_t off = P.off[pi], s = P.s[pi];
+        const uint16_t* g = grads[pi];
+        // run m covers columns off + a_m + [0, 8), a_m = min(8m, s - 8) (s >= 8), or the whole
+        // piece (s < 8); a_m never decreases, so the runs meeting [x0, x1) are a range [lo, hi)
+        const int64_t nrun = s >= kChunk ? (s + kChunk - 1) / kChunk : (s > 0 ? 1 : 0);
+        const int64_t lo = off >= x0 ? 0 : (x0 - off) / kChunk;
+        int64_t hi = off >= x1 ? 0 : (x1 - off + kChunk - 1) / kChunk;  // runs starting before x1 at 8m
+        if (off < x1 && hi >= nrun - 1) hi = nrun;  // the last run starts at or before its nominal 8(nrun - 1)
+        const bool here = g && off >= b_base && off + s <= b_base + b_row && hi > lo;
+        sm[t] = MixMeta{off, s, P.numel[pi], g, lo, int32_t(here ? hi - lo : 0)};
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {  // exclusive scan of the run counts (a handful of parameters per tile)
+        int32_t acc = 0;
+        for (int t = 0; t < int(cnt); ++t) {
+            const int32_t nr = sm[t].run0;
+            sm[t].run0 = acc;
+            acc += nr;
+        }
+        *s_total = acc;
+    }
+    __syncthreads();
+    const int32_t total = *s_total;
+    for (int32_t r = int32_t(threadIdx.x); r < total; r += kBlock) {
+        int lo = 0, hi = int(cnt) - 1;  // last staged parameter whose first run is <= r
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm[mid].run0 <= r) lo = mid; else hi = mid - 1;
+        }
+        const MixMeta m = sm[lo];
+        pack_run<CHECK>(m, m.mlo + (r - m.run0), k0, k1, packed, b_base, b_stride, limit, bad);
+    }
+}
+
+template <bool CHECK>
+__global__ __launch_bounds__(kBlock) void pack_kernel(DevPlan P, int64_t b_base, int64_t b_row, int64_t b_stride,
+                                                      const int64_t* __restrict__ tiles, int64_t n_whole,
+                                                      int64_t n_mixed, const uint16_t* const* __restrict__ grads,
                                                       uint16_t* __restrict__ packed, uint32_t limit,
                                                       int32_t* __restrict__ flag) {
-    __shared__ PackMeta sm[kStageMax];
-    const int64_t n_work = n_tile * n_rg;
+    __shared__ MixMeta sm[kStageMax];
+    __shared__ int32_t s_total;
+    const int64_t n_wrg = (P.nd + kWholeRows - 1) / kWholeRows;
+    const int64_t n_wwork = n_whole * n_wrg;
+    const int64_t n_mrg = (P.nd + kMixRows - 1) / kMixRows;
+    const int64_t n_work = n_wwork + n_mixed * n_mrg;
     bool bad = false;
+    // the mixed items (several rows each, heavier) first, so that they do not form the tail
+    const int64_t n_mwork = n_work - n_wwork;
     for (int64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
-        int64_t jt;
-        if (n_work <= int64_t(UINT32_MAX)) jt = int64_t(uint32_t(w) / uint32_t(n_rg));  // 32-bit divide
-        else jt = w / n_rg;
-        const int64_t k0 = (w - jt * n_rg) * kPackRows;
-        const int64_t kend = k0 + kPackRows < P.nd ? k0 + kPackRows : P.nd;
-        const int64_t j = tile0 + jt;
-        const int64_t x0 = j << kTileShift;
-        const int64_t x = x0 + int64_t(threadIdx.x) * kChunk;
-        // The tile's parameter fields, read once per block (scalar loads; index clamped into
-        // range): the dependent chain is tile map -> fields and pointer -> data.
-        const int64_t iu = ld_const(P.tile_first, j);
-        const int64_t ic = iu < P.n ? iu : P.n - 1;
-        const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
-        const int64_t s = ld_const(P.s, ic), numel = ld_const(P.numel, ic);
-        const uint16_t* g = ld_const(grads, ic);
-        const bool whole = iu < P.n && off <= x0 && end >= x0 + kTileCols;
-        if (whole && !g) continue;  // the whole tile belongs to a parameter without a gradient
-        if (whole && aligned16(g)) {
-            const int64_t c = x - off;
-            const bool direct = ((s | off) & 7) == 0;  // every source chunk 16-byte aligned
-            uint16_t* dst = packed + (x - b_base);
-            uint4 v[kPackRows];
-#pragma unroll
-            for (int u = 0; u < kPackRows; ++u) {
-                const int64_t k = k0 + u;
-                if (k >= kend) break;
-                const int64_t e0 = k * s + c;
-                if (e0 + kChunk <= numel) {
-                    v[u] = direct ? load16(g + e0) : load8_realigned(g, e0);
-                } else {
-                    const ZS_GLOBAL uint16_t* gg = gptr(g);
-                    uint16_t h[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) h[t] = (e0 + t < numel) ? gg[e0 + t] : uint16_t(0);
-                    v[u] = pack8(h);
-                }
-                if constexpr (CHECK) bad |= out_of_range8(v[u], limit);
-            }
-#pragma unroll
-            for (int u = 0; u < kPackRows; ++u) {
-                const int64_t k = k0 + u;
-                if (k >= kend) break;
-                store16(dst + k * b_stride, v[u]);
-            }
+        if (w >= n_mwork) {
+            const WholeItem it = whole_item(P, tiles, grads, w - n_mwork, n_wrg, n_whole);
+            if (!it.g) continue;  // no gradient this step
+            uint4 v[kWholeRows];
+            whole_loads<CHECK>(P, it, v, limit, bad);
+            whole_stores(P, it, v, packed, b_base, b_stride);
             continue;
         }
-        // parameters overlapping the tile: [iu, last], last = the tile map's next entry (clamped)
-        const int64_t inext = ld_const(P.tile_first, j + 1);
-        const int64_t last = inext < P.n ? inext : P.n - 1;
-        const int64_t cnt = iu < P.n ? last - iu + 1 : 0;
-        if (cnt <= kStageMax) {
-            __syncthreads();  // the previous iteration's readers are done with the stage
-            for (int64_t t = threadIdx.x; t < cnt; t += kBlock) {
-                const int64_t pi = iu + t;
-                sm[t] = PackMeta{P.off[pi], P.end[pi], P.s[pi], P.numel[pi], grads[pi]};
-            }
-            __syncthreads();
-            if (x < b_base || x >= b_base + b_stride) continue;
-            const int t0 = staged_search(sm, int(cnt), x);
-            for (int64_t k = k0; k < kend; ++k)
-                pack_chunk_staged<CHECK>(sm, int(cnt), t0, k, x, packed + k * b_stride + (x - b_base), limit, bad);
-            continue;
-        }
-        if (x < b_base || x >= b_base + b_stride) continue;
-        const int64_t i = param_of_column(P, x);
-        for (int64_t k = k0; k < kend; ++k)
-            pack_chunk_generic<CHECK>(P, i, k, x, grads, packed + k * b_stride + (x - b_base), limit, bad);
+        const int64_t kg = w / n_mixed;
+        pack_mixed_item<CHECK>(P, sm, &s_total, b_base, b_row, b_stride, tiles, n_whole + (w - kg * n_mixed), kg,
+                               grads, packed, limit, bad);
     }
     if constexpr (CHECK) flag_wave(bad, flag);
 }
@@ -265,9 +318,10 @@ __device__ __forceinline__ uint4 merge_split(const uint4& a, const uint4& b, int
 
 // One chunk of parameter fields (numel, s, column of the slice in the rows, 1/s, chunk base).
 // Element e0..e0+7 of the parameter: row k = e0 / s, column j0 = e0 mod s.  A chunk inside one
-// row is one realigned load; a chunk crossing into the next row (s >= 8) is two realigned
-// loads and a merge (a crossing chunk is never in the last row, so both loads stay inside
-// the block); the tail of a parameter and rows shorter than 8 go element by element.
+// row is one 16-byte load at the row's alignment; a chunk crossing into the next row (s >= 8)
+// is two loads and a merge (a crossing chunk is never in the last row, so both loads stay
+// inside the block); the tail of a parameter and rows shorter than 8 go element by element.
+// The store is one 16-byte store whatever the output's 2-byte alignment.
 __device__ __forceinline__ void unpack_chunk(int64_t u, int64_t ucb, int64_t numel, int64_t s, int64_t col,
                                              double inv_s, int64_t b_stride, const uint16_t* __restrict__ gathered,
                                              uint16_t* out) {
@@ -276,15 +330,15 @@ __device__ __forceinline__ void unpack_chunk(int64_t u, int64_t ucb, int64_t num
     int64_t k = int64_t(double(e0) * inv_s);
     int64_t j0 = e0 - k * s;
     if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
-    if (e0 + kChunk <= numel && aligned16(out)) {
+    if (e0 + kChunk <= numel) {
         if (j0 + kChunk <= s) {
-            store16(out + e0, load8_realigned(gathered, k * b_stride + col + j0));
+            store16_any(out + e0, load16_any(gathered + k * b_stride + col + j0));
             return;
         }
         if (s >= kChunk) {
-            const uint4 a = load8_realigned(gathered, k * b_stride + col + j0);
-            const uint4 b = load8_realigned(gathered, (k + 1) * b_stride + col);
-            store16(out + e0, merge_split(a, b, int(s - j0)));
+            const uint4 a = load16_any(gathered + k * b_stride + col + j0);
+            const uint4 b = load16_any(gathered + (k + 1) * b_stride + col);
+            store16_any(out + e0, merge_split(a, b, int(s - j0)));
             return;
         }
     }
@@ -327,7 +381,7 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_bas
             // Rows at least as long as the group: find the group's first row once per block;
             // each thread's chunk is then in that row or the next.
             constexpr int64_t kSpanElems = kUnpackUnroll * kUTileChunks * kChunk;
-            if (s >= kSpanElems && aligned16(out)) {
+            if (s >= kSpanElems) {
                 const int64_t es = (ua - ucb) * kChunk;
                 int64_t ks = int64_t(double(es) * inv_s);
                 int64_t js = es - ks * s;
@@ -339,7 +393,7 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(DevPlan P, int64_t b_bas
                     int64_t j0 = js + d, k = ks;
                     if (j0 >= s) { j0 -= s; ++k; }
                     if (e0 + kChunk <= numel && j0 + kChunk <= s)
-                        store16(out + e0, load8_realigned(gathered, k * b_stride + col + j0));
+                        store16_any(out + e0, load16_any(gathered + k * b_stride + col + j0));
                     else
                         unpack_chunk(ua + t * kUTileChunks + threadIdx.x, ucb, numel, s, col, inv_s, b_stride,
                                      gathered, out);
@@ -444,20 +498,21 @@ static zero_status pack_common(const zero_plan* plan, int64_t b, const void* con
     if (stride == 0) return ZERO_OK;  // empty rows: nothing to read or write, buffers may be NULL
     if (!d_grad_ptrs || !d_packed || (check && !d_flag)) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
     if (!host_aligned16(d_packed)) return fail(ZERO_EINVAL, "%s: packed buffer not 16-byte aligned", who);
-    const int64_t tile0 = base >> kTileShift;
-    const int64_t n_tile = ((base + stride + kTileCols - 1) >> kTileShift) - tile0;
-    const int64_t n_rg = (plan->nd + kPackRows - 1) / kPackRows;
-    const int g = grid_for(n_tile * n_rg);
+    const int64_t* pt = plan->h_ptile + 3 * b;
+    const int64_t* tiles = plan->d_ptiles + 2 * pt[0];
+    const int64_t n_whole = pt[1], n_mixed = pt[2];
+    const int g = grid_for(n_whole * ((plan->nd + kWholeRows - 1) / kWholeRows) +
+                           n_mixed * ((plan->nd + kMixRows - 1) / kMixRows));
     hipStream_t s = (hipStream_t)stream;
     const uint16_t* const* grads = reinterpret_cast<const uint16_t* const*>(d_grad_ptrs);
     uint16_t* packed = static_cast<uint16_t*>(d_packed);
     const uint32_t limit = check ? check_limit_bits(plan->dtype, plan->nd) : 0u;
     if (!check)
-        pack_kernel<false><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed, limit,
-                                                nullptr);
+        pack_kernel<false><<<g, kBlock, 0, s>>>(plan->dev, base, br[BF_ROW], stride, tiles, n_whole, n_mixed, grads,
+                                                packed, limit, nullptr);
     else
-        pack_kernel<true><<<g, kBlock, 0, s>>>(plan->dev, base, stride, tile0, n_tile, n_rg, grads, packed, limit,
-                                               d_flag);
+        pack_kernel<true><<<g, kBlock, 0, s>>>(plan->dev, base, br[BF_ROW], stride, tiles, n_whole, n_mixed, grads,
+                                               packed, limit, d_flag);
     return check_launch(who);
 }
 

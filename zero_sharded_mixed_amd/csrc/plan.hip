@@ -227,6 +227,7 @@ extern "C" void zero_plan_destroy(zero_plan* plan) {
     free(plan->h_param);
     free(plan->h_bucket);
     free(plan->h_bucket_chunks);
+    free(plan->h_ptile);
     delete plan;
 }
 
@@ -291,6 +292,8 @@ extern "C" zero_status zero_plan_create_grouped(const int64_t* numels, const int
         for (int64_t i = 0; i < n; ++i) chunks_bound += (numels[i] + 7) / 8;
         const int64_t utiles_bound = chunks_bound / kUTileChunks + 2;
         const size_t o_tile = take(4 * size_t(tiles_bound)), o_utile = take(4 * size_t(utiles_bound));
+        // every bucket's tiles (a tile shared by two buckets is listed for both)
+        const size_t o_ptile = take(16 * size_t(tiles_bound + n + 2));
 
         ZS_HIP(hipGetDevice(&P->device), "hipGetDevice");
         ZS_HIP(hipMalloc(&P->d_mem, bytes), "hipMalloc(plan tables)");
@@ -323,6 +326,7 @@ extern "C" zero_status zero_plan_create_grouped(const int64_t* numels, const int
         P->d_adam_const = (float*)(m + o_const);
         int32_t* d_tile = (int32_t*)(m + o_tile);
         int32_t* d_utile = (int32_t*)(m + o_utile);
+        P->d_ptiles = (int64_t*)(m + o_ptile);
 
         hipStream_t s = nullptr;
         ZS_HIP(hipMemcpy(d_numels_in, numels, 8 * size_t(n), hipMemcpyHostToDevice), "upload numels");
@@ -406,6 +410,46 @@ extern "C" zero_status zero_plan_create_grouped(const int64_t* numels, const int
                     u += (P->h_param[i * kParamFields + PF_NUMEL] + kChunk - 1) / kChunk;
                 P->h_bucket_chunks[2 * b + 1] = u;
             }
+        }
+
+        // Tile lists of the pack: per bucket, the tiles of [O_b, O_b + L_b) that lie inside one
+        // parameter, then the others.  Parameters are in shard order, so one walk suffices.
+        {
+            const int64_t nb = P->n_buckets;
+            P->h_ptile = (int64_t*)calloc(size_t(3 * nb), 8);
+            if (!P->h_ptile) { st = fail(ZERO_ENOMEM, "zero_plan_create: host tables"); goto done; }
+            std::vector<int64_t> whole, mixed, all;  // (tile, first parameter ending after its start)
+            int64_t i = 0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const int64_t* r = P->h_bucket + b * kBucketFields;
+                whole.clear();
+                mixed.clear();
+                if (r[BF_STRIDE] > 0) {
+                    const int64_t j0 = r[BF_BASE] >> kTileShift, j1 = (r[BF_BASE] + r[BF_STRIDE] - 1) >> kTileShift;
+                    for (int64_t j = j0; j <= j1; ++j) {
+                        const int64_t x0 = j << kTileShift;
+                        while (i < n && P->h_param[i * kParamFields + PF_OFFSET] + P->h_param[i * kParamFields + PF_SHARD] <= x0)
+                            ++i;  // first parameter whose range ends after x0
+                        const bool in_one = i < n && P->h_param[i * kParamFields + PF_OFFSET] <= x0 &&
+                                            P->h_param[i * kParamFields + PF_OFFSET] +
+                                                    P->h_param[i * kParamFields + PF_SHARD] >= x0 + kTileCols;
+                        std::vector<int64_t>& to = in_one ? whole : mixed;
+                        to.push_back(j);
+                        to.push_back(i);
+                    }
+                }
+                P->h_ptile[3 * b] = int64_t(all.size() / 2);
+                P->h_ptile[3 * b + 1] = int64_t(whole.size() / 2);
+                P->h_ptile[3 * b + 2] = int64_t(mixed.size() / 2);
+                all.insert(all.end(), whole.begin(), whole.end());
+                all.insert(all.end(), mixed.begin(), mixed.end());
+            }
+            if (int64_t(all.size() / 2) > tiles_bound + n + 2) {
+                st = fail(ZERO_EHIP, "zero_plan_create: tile lists beyond their bound");
+                goto done;
+            }
+            if (!all.empty())
+                ZS_HIP(hipMemcpy(P->d_ptiles, all.data(), 8 * all.size(), hipMemcpyHostToDevice), "upload tile lists");
         }
 
         DevPlan& D = P->dev;

@@ -118,28 +118,18 @@ __device__ __forceinline__ void store4f(float* p, const float4& v) {
     *gptr(reinterpret_cast<zs_f32x4*>(p)) = w;
 }
 
-// Eight consecutive 16-bit elements starting at element e of a 16-byte aligned buffer,
-// assembled from the aligned 16-byte granules that hold them (never a granule that holds
-// none of the eight).  Branch-free: the d = e mod 8 element shift is a selection of 32-bit
-// words by d/2 followed by a 2-byte funnel shift when d is odd.
-__device__ __forceinline__ uint4 load8_realigned(const uint16_t* __restrict__ base, int64_t e) {
-    const int64_t q = e >> 3;
-    const int d = int(e & 7);
-    const uint4 a = load16(base + 8 * q);
-    if (d == 0) return a;
-    const uint4 b = load16(base + 8 * q + 8);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    const int h = d >> 1;
-    const uint32_t sh = (d & 1) ? 2u : 0u;
-    uint32_t lo[5];
-#pragma unroll
-    for (int t = 0; t < 5; ++t) {  // lo[t] = w[h + t] (h in 0..3, h + t <= 7)
-        const uint32_t c0 = w[t], c1 = w[t + 1 < 8 ? t + 1 : 7], c2 = w[t + 2 < 8 ? t + 2 : 7],
-                       c3 = w[t + 3 < 8 ? t + 3 : 7];
-        lo[t] = h == 0 ? c0 : h == 1 ? c1 : h == 2 ? c2 : c3;
-    }
-    return make_uint4(__builtin_amdgcn_alignbyte(lo[1], lo[0], sh), __builtin_amdgcn_alignbyte(lo[2], lo[1], sh),
-                      __builtin_amdgcn_alignbyte(lo[3], lo[2], sh), __builtin_amdgcn_alignbyte(lo[4], lo[3], sh));
+// Sixteen bytes from any 2-byte aligned address: one global_load_dwordx4, the memory system
+// handling the misalignment (measured on MI355X: unaligned 16-byte loads of a streaming copy
+// run at the aligned rate and return the bytes at the exact address).
+typedef zs_u32x4 zs_u32x4_a2 __attribute__((aligned(2)));
+__device__ __forceinline__ uint4 load16_any(const uint16_t* p) {
+    const zs_u32x4_a2 w = *(const ZS_GLOBAL zs_u32x4_a2*)p;
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
+__device__ __forceinline__ void store16_any(uint16_t* p, const uint4& v) {
+    zs_u32x4_a2 w = {v.x, v.y, v.z, v.w};
+    *(ZS_GLOBAL zs_u32x4_a2*)p = w;
 }
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -263,6 +253,13 @@ struct zero_plan {
     int64_t* h_param = nullptr;   // n * kParamFields
     int64_t* h_bucket = nullptr;  // n_buckets * kBucketFields
     int64_t* h_bucket_chunks = nullptr;  // [n_buckets][2]: the bucket's unpack chunk range [u0, u1)
+    // Shard tiles of every bucket, split by kind: [n_buckets][3] = offset into d_ptiles (in
+    // entries), tiles that lie inside one parameter ("whole"), then tiles holding several
+    // parameters, padding or the row gap ("mixed"); d_ptiles lists each bucket's whole tiles,
+    // then its mixed ones, one entry = (tile index, first parameter whose range ends after the
+    // tile's first column) as two int64.
+    int64_t* h_ptile = nullptr;
+    int64_t* d_ptiles = nullptr;
     // device tables
     void* d_mem = nullptr;        // one allocation holding every table below
     zs::DevPlan dev{};
