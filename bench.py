@@ -314,9 +314,11 @@ def run_zero3(w, ctx, steps, warmup, device, graph=True, prefetch=False):
     pass gathers all but the last layer again and reduce-scatters each layer's gradients (pack
     + reduce) right after it, then Adam writes this rank's 16-bit shard.  Full emulation: every
     virtual rank's gradients are packed for the per-layer buckets beforehand; this rank's are
-    re-packed inside each timed step, into the rows the reduce reads.  All on one stream; with
-    prefetch=True also with the gathers on a second stream into two scratch buffers.  With
-    graph=True each step (about 200 launches) is also captured into a HIP graph and replayed."""
+    re-packed inside each timed step, into the rows the reduce reads.  All on one stream, each
+    backward step one zero_z3_layer_step launch; `separate_launches` times the same step with a
+    launch per piece (and `speedup` = its time / the fused schedule's); with prefetch=True also
+    with the gathers on a second stream into two scratch buffers.  With graph=True each step is
+    also captured into a HIP graph and replayed."""
     import workloads as W
 
     st2, live = ctx.st, ctx.live
@@ -400,16 +402,22 @@ def run_zero3(w, ctx, steps, warmup, device, graph=True, prefetch=False):
             del g
         return res
 
-    z3 = Z.Zero3Schedule(z)
+    z3 = Z.Zero3Schedule(z, fused=True)
     torch.cuda.synchronize()
     log(f"[bench] zero3: {len(z.buckets)} layer buckets, scratch {z3.scratch.numel()} elements "
         f"({time.time() - t0:.1f}s)")
     out = measure(z3)
+    out["schedule"] = "one stream; each backward step one launch (reduce l+1, pack l, gather l-1)"
+    del z3
+    z3 = Z.Zero3Schedule(z)  # the same step with three launches per backward layer
+    sep = measure(z3)
+    sep["speedup"] = round(sep["ms_per_step"] / out["ms_per_step"], 3)
+    out["separate_launches"] = sep
     del z3
     if prefetch:  # the gathers on a second stream into two scratch buffers
         z3 = Z.Zero3Schedule(z, prefetch=True)
         pf = measure(z3)
-        pf["speedup"] = round(out["ms_per_step"] / pf["ms_per_step"], 3)
+        pf["speedup"] = round(pf["ms_per_step"] / out["ms_per_step"], 3)
         out["prefetch"] = pf
         del z3
     del packed_all, z

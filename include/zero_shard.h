@@ -376,6 +376,29 @@ zero_status zero_reduce_adam_bucket(const zero_plan* plan, int64_t b, const void
                                     const uint8_t* d_live, float* d_p32, float* d_m, float* d_v,
                                     const int32_t* d_flag, void* d_arena, void* stream);
 
+/* ------------------------------------------------------- ZeRO-3 layer step ------ */
+
+/* One launch holding up to three independent pieces of ZeRO-3's per-layer traffic [Z3: each
+ * layer's parameters are all-gathered before it runs and freed after it; in the backward pass,
+ * layers L-1 .. 0, each layer's gradients are reduce-scattered once its backward has run]:
+ *   reduce_b >= 0:  zero_reduce_shard(plan, reduce_b, d_rows, row_stride, d_live, d_g32, d_flag)
+ *   pack_b   >= 0:  zero_pack_bucket(plan, pack_b, d_grad_ptrs, d_packed), or with check != 0
+ *                   zero_pack_bucket_check(..., d_flag)
+ *   gather_b >= 0:  zero_unpack(plan, gather_b, d_gathered, d_param_ptrs)
+ * (-1 = that piece is absent; its pointers are not read).  Each piece computes exactly what its
+ * own entry point computes, with the same arguments, errors and conventions; the pieces share
+ * the grid and run concurrently, so no piece may read or write what another writes.  With one
+ * bucket per layer (zero_plan_create_grouped), a backward step of layer l is reduce_b = l + 1,
+ * pack_b = l, gather_b = l - 1: the reduce reads rows packed one step earlier, the pack reads the
+ * gradients layer l just produced, the gather fills the scratch that layer l no longer needs --
+ * one launch (and one launch tail) per layer instead of three.
+ * Errors: as the three entry points (the first failing piece's), and ZERO_EINVAL for an index
+ * below -1. */
+zero_status zero_z3_layer_step(const zero_plan* plan, int64_t reduce_b, const void* d_rows, int64_t row_stride,
+                               const uint8_t* d_live, float* d_g32, int64_t pack_b, const void* const* d_grad_ptrs,
+                               void* d_packed, int32_t check, int64_t gather_b, const void* d_gathered,
+                               void* const* d_param_ptrs, int32_t* d_flag, void* stream);
+
 /* ------------------------------------------------------- dynamic loss scaling ------ */
 
 /* Write the host configuration *cfg (every field, good_steps and overflows included) to the

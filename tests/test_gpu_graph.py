@@ -116,9 +116,10 @@ def _release():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("prefetch", [False, True])
+@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused"])
 @pytest.mark.parametrize("nd,rank", [(8, 3), (64, 17)])
-def test_captured_zero3_step_replays_like_eager_steps(nd, rank, prefetch):
+def test_captured_zero3_step_replays_like_eager_steps(nd, rank, mode):
+    prefetch = mode == "prefetch"
     """A whole ZeRO-3 step (forward gathers, backward gathers with each layer's pack + reduce,
     Adam) of a 5-layer model, captured once and replayed; with prefetch the capture spans the
     caller's stream and the gather stream."""
@@ -145,7 +146,7 @@ def test_captured_zero3_step_replays_like_eager_steps(nd, rank, prefetch):
     gptrs = Z.ptr_table([to_dev16(random_bits(rng, x) & np.uint16(0xBBFF)) if l else None
                          for x, l in zip(numels, live)])
     rows = [to_dev16(random_bits(rng, nd * int(bk.row_stride)) & np.uint16(0xBBFF)) for bk in st.buckets]
-    z3 = Z.Zero3Schedule(st, prefetch=prefetch)
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused")
     out = torch.zeros_like(st.packed)
 
     def rows_of(lid):
@@ -180,5 +181,5 @@ def test_captured_zero3_step_replays_like_eager_steps(nd, rank, prefetch):
         torch.cuda.synchronize()
         _ = (st.p32 * 2).sum().item()
         for j, (a, b) in enumerate(zip(bufs, eager[i])):
-            assert torch.equal(a, b), (nd, rank, prefetch, i, j)
-    say(f"zero3 graph nd={nd} prefetch={prefetch}: 3 replays match 3 eager steps")
+            assert torch.equal(a, b), (nd, rank, mode, i, j)
+    say(f"zero3 graph nd={nd} {mode}: 3 replays match 3 eager steps")

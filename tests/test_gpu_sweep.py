@@ -234,7 +234,7 @@ def test_random_plan_overflow_skips(seed):
 @pytest.mark.parametrize("seed", range(16))
 def test_random_zero3_schedule(seed):
     """Random layered models (1 to 12 layers of 1 to 6 parameters, empty ones included) through
-    ZeRO-3's schedule, one stream or prefetch: every gather (forward and backward) against the
+    ZeRO-3's schedule (one stream, prefetch, or the fused layer steps): every gather (forward and backward) against the
     oracle's unpack, the gather order, each layer's packed gradients, the reduced shard and flag,
     then Adam, against the oracle."""
     rng = np.random.default_rng(20_000 + seed)
@@ -249,8 +249,9 @@ def test_random_zero3_schedule(seed):
                           int(rng.integers(1, 30000)))
             groups.append(layer)
     dtype = BF16 if rng.random() < 0.5 else FP16
-    prefetch = bool(rng.random() < 0.5)
-    say(f"zero3 sweep seed={seed} nd={nd} rank={rank} layers={n_layers} n={len(numels)} prefetch={prefetch}")
+    mode = ("one-stream", "prefetch", "fused")[int(rng.integers(0, 3))]
+    prefetch = mode == "prefetch"
+    say(f"zero3 sweep seed={seed} nd={nd} rank={rank} layers={n_layers} n={len(numels)} {mode}")
     st = Z.ShardStep(numels, nd, rank, 0, dtype, groups=groups)
     pl = oracle.plan(numels, nd, rank, 0, np.array(groups, np.int32))
     assert pl.n_buckets == n_layers
@@ -267,7 +268,7 @@ def test_random_zero3_schedule(seed):
     steps = np.zeros(len(numels), np.int32)
     live = (rng.random(len(numels)) > 0.2).astype(np.uint8)
     st.live.copy_(torch.from_numpy(live))
-    z3 = Z.Zero3Schedule(st, prefetch=prefetch)
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused")
 
     def check_gather(lid, params):
         outs = [np.zeros(x, np.uint16) for x in numels]

@@ -50,9 +50,10 @@ def test_grouped_plan_tables(nd, cap, seed):
         assert np.all(members == members[0])  # a bucket never spans two runs of ids
 
 
-@pytest.mark.parametrize("prefetch", [False, True])
+@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused"])
 @pytest.mark.parametrize("nd,rank,dtype", [(8, 3, BF16), (64, 17, FP16)])
-def test_zero3_step_matches_oracle(nd, rank, dtype, prefetch):
+def test_zero3_step_matches_oracle(nd, rank, dtype, mode):
+    prefetch = mode == "prefetch"
     n_layers, d, vocab = 3, 48, 500
     numels, groups = layered_model(n_layers, d, vocab)
     say(f"zero3 nd={nd} rank={rank} layers={n_layers + 2}")
@@ -75,7 +76,7 @@ def test_zero3_step_matches_oracle(nd, rank, dtype, prefetch):
     live = np.ones(len(numels), np.uint8)
     live[[3, 4]] = 0  # two parameters of layer 1 without a gradient (the layer-drop mapping)
     st.live.copy_(torch.from_numpy(live))
-    z3 = Z.Zero3Schedule(st, prefetch=prefetch)
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused")
 
     def check_gather(lid, params):
         outs = [np.zeros(x, np.uint16) for x in numels]
@@ -124,8 +125,9 @@ def test_zero3_step_matches_oracle(nd, rank, dtype, prefetch):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("prefetch", [False, True])
-def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(prefetch):
+@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused"])
+def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(mode):
+    prefetch = mode == "prefetch"
     """The GPT-2 1.5B-shaped list at Nd = 8 with one bucket per layer, as bench.py's ZeRO-3 leg
     runs it: every forward gather restores its layer's parameters exactly; after the step,
     p32 / m / v and this rank's 16-bit shard equal the ZeRO-2 step's (same gradients, 500M-element
@@ -177,7 +179,7 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(prefetch):
     hp = (w.lr, w.betas[0], w.betas[1], w.eps, w.grad_scale)
     A.adam(*hp)
     # ZeRO-3
-    z3 = Z.Zero3Schedule(G, prefetch=prefetch)
+    z3 = Z.Zero3Schedule(G, prefetch=prefetch, fused=mode == "fused")
 
     def restored(lid, params):
         for i, view in zip(z3.layers[lid], params):
@@ -212,3 +214,23 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(prefetch):
     assert_close_f32(to_np32(G.v[cols_dev]), np.array([x[2] for x in want], np.float32), "v")
     del pa, pg, own, lp, A, G, z3
     torch.cuda.empty_cache()
+
+
+def test_z3_layer_step_arguments():
+    """zero_z3_layer_step: no piece = nothing to do; an index below -1 or past the last bucket is
+    refused before anything runs; the pieces keep their own entry points' checks."""
+    st = Z.ShardStep([1000, 37, 5000], 8, 3, 0, Z.ZERO_BF16, groups=[0, 1, 2])
+    Z.zero_z3_layer_step(st.plan)
+    for kw in (dict(reduce_b=-2), dict(pack_b=-3), dict(gather_b=-2)):
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_z3_layer_step(st.plan, **kw)
+        assert e.value.status == Z.ZERO_EINVAL
+    ptrs = Z.ptr_table([torch.zeros(x, dtype=torch.int16, device=DEV) for x in (1000, 37, 5000)])
+    with pytest.raises(Z.ZeroError) as e:  # bucket out of range (the pack's own check)
+        Z.zero_z3_layer_step(st.plan, pack_b=3, grad_ptrs=ptrs, packed=st.packed)
+    assert e.value.status == Z.ZERO_EINVAL
+    with pytest.raises(Z.ZeroError) as e:  # the checked pack needs the flag
+        Z.zero_z3_layer_step(st.plan, pack_b=0, grad_ptrs=ptrs, packed=st.block(st.packed, 0), check=True)
+    assert e.value.status == Z.ZERO_EINVAL
+    torch.cuda.synchronize()
+    assert int(st.flag.item()) == 0 and torch.all(st.packed == 0)

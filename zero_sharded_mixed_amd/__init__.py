@@ -11,7 +11,7 @@ from ._binding import (EXPORTS, LIB_PATH, LOSS_SCALER_BYTES, ZERO_BF16, ZERO_EHI
                        zero_pack_bucket, zero_pack_bucket_check, zero_param_info, zero_plan_bucket_info,
                        zero_plan_create, zero_plan_create_grouped, zero_plan_destroy, zero_plan_get_summary,
                        zero_plan_model_state_bytes, zero_plan_param_info, zero_plan_summary, zero_reduce_adam_bucket,
-                       zero_reduce_shard, zero_shard_init, zero_unpack)
+                       zero_reduce_shard, zero_shard_init, zero_unpack, zero_z3_layer_step)
 from .step import ShardStep, Zero3Schedule
 
 __all__ = ["EXPORTS", "LIB_PATH", "LOSS_SCALER_BYTES", "Plan", "ShardStep", "Zero3Schedule", "ZeroError", "lib",
@@ -21,5 +21,5 @@ __all__ = ["EXPORTS", "LIB_PATH", "LOSS_SCALER_BYTES", "Plan", "ShardStep", "Zer
            "zero_overflow_check", "zero_pack_bucket", "zero_pack_bucket_check", "zero_param_info",
            "zero_plan_bucket_info", "zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy",
            "zero_plan_get_summary", "zero_plan_model_state_bytes", "zero_plan_param_info", "zero_plan_summary",
-           "zero_reduce_adam_bucket", "zero_reduce_shard", "zero_shard_init", "zero_unpack", "ZERO_BF16", "ZERO_FP16",
+           "zero_reduce_adam_bucket", "zero_reduce_shard", "zero_shard_init", "zero_unpack", "zero_z3_layer_step", "ZERO_BF16", "ZERO_FP16",
            "ZERO_OK", "ZERO_EINVAL", "ZERO_ENOMEM", "ZERO_EHIP", "ZERO_ERANGE"]

@@ -26,7 +26,8 @@ EXPORTS = ("zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy", 
            "zero_plan_param_info", "zero_plan_bucket_info", "zero_model_state_bytes", "zero_plan_model_state_bytes",
            "zero_pack_bucket", "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack",
            "zero_shard_init", "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket",
-           "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_last_error", "zero_adam_step_noalloc")
+           "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_last_error", "zero_adam_step_noalloc",
+           "zero_z3_layer_step")
 ADAM_NOALLOC_MAX_PARAMS = 131072  # ZERO_ADAM_NOALLOC_MAX_PARAMS
 
 
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
         "zero_adam_step": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
         "zero_adam_step_noalloc": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
         "zero_unpack": (i32, [vp, i64, vp, vp, vp]),
+        "zero_z3_layer_step": (i32, [vp, i64, vp, i64, vp, vp, i64, vp, vp, i32, i64, vp, vp, vp, vp]),
         "zero_shard_init": (i32, [vp, vp, i32, vp, vp]),
         "zero_pack_bucket_check": (i32, [vp, i64, vp, vp, vp, vp]),
         "zero_adam_prepare": (i32, [vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp]),
@@ -368,6 +370,30 @@ def zero_unpack(plan: Plan, b: int, gathered: torch.Tensor, param_ptrs: torch.Te
     _check(lib().zero_unpack(plan.handle, b, _buf(plan, gathered, "zero_unpack: gathered", plan.block_elems(b),
                                                   elem_size=2),
                              _table(plan, param_ptrs, "zero_unpack: parameters", 2), _stream(stream)))
+
+
+def zero_z3_layer_step(plan: Plan, reduce_b: int = -1, rows: Optional[torch.Tensor] = None, row_stride: int = 0,
+                       live: Optional[torch.Tensor] = None, g32: Optional[torch.Tensor] = None, pack_b: int = -1,
+                       grad_ptrs: Optional[torch.Tensor] = None, packed: Optional[torch.Tensor] = None,
+                       check: bool = False, gather_b: int = -1, gathered: Optional[torch.Tensor] = None,
+                       param_ptrs: Optional[torch.Tensor] = None, flag: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """reduce of bucket reduce_b, pack of bucket pack_b and unpack of bucket gather_b in one launch
+    (an index of -1 leaves that piece out; its buffers are then not needed)."""
+    w = "zero_z3_layer_step"
+    r = reduce_b >= 0
+    k = pack_b >= 0
+    u = gather_b >= 0
+    _check(lib().zero_z3_layer_step(
+        plan.handle, reduce_b,
+        _buf(plan, rows, w + ": rows", plan.rows_elems(reduce_b, row_stride), elem_size=2) if r else None, row_stride,
+        _buf(plan, live, w + ": live", plan.n, U8) if r else None,
+        _buf(plan, g32, w + ": g32", plan.shard_numel, F32) if r else None, pack_b,
+        _table(plan, grad_ptrs, w + ": gradients", 2) if k else None,
+        _buf(plan, packed, w + ": packed", plan.block_elems(pack_b), elem_size=2) if k else None, int(bool(check)),
+        gather_b, _buf(plan, gathered, w + ": gathered", plan.block_elems(gather_b), elem_size=2) if u else None,
+        _table(plan, param_ptrs, w + ": parameters", 2) if u else None,
+        _buf(plan, flag, w + ": flag", 1, I32), _stream(stream)))
 
 
 def zero_shard_init(plan: Plan, src_ptrs: torch.Tensor, src_dtype: int, p32: torch.Tensor, stream=None) -> None:

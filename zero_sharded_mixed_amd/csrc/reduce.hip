@@ -10,62 +10,16 @@
 // ranks are issued ahead of the adds (kAhead rows in flight) so HBM latency overlaps.
 // Columns of parameters without a gradient are skipped before any row is read.  The overflow
 // flag is ORed once per wavefront (a ballot, then one atomic), only when a value is found.
-#include "zs_common.h"
+#include "zs_reduce.h"
 
 namespace zs {
-
-#ifndef ZS_REDUCE_TILES
-#define ZS_REDUCE_TILES 1
-#endif
-constexpr int kReduceTiles = ZS_REDUCE_TILES;  // consecutive tiles per block (one chunk of each per thread)
-
-template <int DT>
-__device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, int64_t c, unsigned mask,
-                                             const uint16_t* __restrict__ rows, int64_t row_stride,
-                                             float* __restrict__ g32, bool& bad) {
-    float acc[8];
-    reduce_rows8<DT>(rows + c, P.nd, row_stride, acc);
-    float* dst = g32 + x;
-    if (mask == 0xffu) {
-        store4f(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
-        store4f(dst + 4, make_float4(acc[4], acc[5], acc[6], acc[7]));
-    } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            if (mask & (1u << t)) gptr(dst)[t] = acc[t];
-    }
-    bad |= any_bad8(acc, mask);
-}
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_base, int64_t b_row, int64_t tile0,
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
-    const int64_t n_groups = (n_tile + kReduceTiles - 1) / kReduceTiles;
-    bool bad = false;
-    for (int64_t w = blockIdx.x; w < n_groups; w += gridDim.x) {
-        const int64_t j = tile0 + w * kReduceTiles;
-        const int64_t x0 = j << kTileShift;
-        // block-uniform (scalar loads): does the whole group of tiles lie inside one parameter,
-        // hence inside this bucket, and is that parameter live?
-        const int64_t iu = ld_const(P.tile_first, j);
-        const int64_t ic = iu < P.n ? iu : P.n - 1;
-        const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
-        const bool lv = ld_const(live, ic) != 0;
-        const bool whole = iu < P.n && off <= x0 && end >= x0 + kReduceTiles * kTileCols;
-        if (whole && !lv) continue;
-#pragma unroll
-        for (int t = 0; t < kReduceTiles; ++t) {
-            const int64_t x = x0 + t * kTileCols + int64_t(threadIdx.x) * kChunk;
-            const int64_t c = x - b_base;
-            if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
-            const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
-            if (mask == 0) continue;
-            reduce_chunk<DT>(P, x, c, mask, rows, row_stride, g32, bad);
-        }
-    }
-    if (flag) flag_wave(bad, flag);
+    reduce_body<DT>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,
@@ -88,31 +42,43 @@ __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float
 
 using namespace zs;
 
+namespace zs {
+zero_status reduce_prepare(const zero_plan* plan, int64_t b, const void* d_rows, int64_t row_stride,
+                           const uint8_t* d_live, float* d_g32, int32_t* d_flag, const char* who, ReduceLaunch* out) {
+    *out = ReduceLaunch{};
+    if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "%s: bucket %lld out of range", who, (long long)b);
+    const int64_t* br = plan->h_bucket + b * kBucketFields;
+    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
+    if (row == 0) return ZERO_OK;  // empty rows: nothing to read or write, buffers may be NULL
+    if (!d_rows || !d_live || !d_g32) return fail(ZERO_EINVAL, "%s: NULL pointer", who);
+    if (!host_aligned16(d_rows) || !host_aligned16(d_g32))
+        return fail(ZERO_EINVAL, "%s: rows and g32 must be 16-byte aligned", who);
+    if (row_stride < stride || row_stride % kChunk != 0)
+        return fail(ZERO_EINVAL, "%s: row_stride %lld must be >= %lld and a multiple of 8", who, (long long)row_stride,
+                    (long long)stride);
+    const int64_t tile0 = base >> kTileShift;
+    const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
+    *out = ReduceLaunch{base, row, tile0, n_tile, static_cast<const uint16_t*>(d_rows), row_stride, d_live, d_g32,
+                        d_flag, reduce_blocks(n_tile)};
+    return ZERO_OK;
+}
+}  // namespace zs
+
 extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const void* d_rows, int64_t row_stride,
                                          const uint8_t* d_live, float* d_g32, int32_t* d_flag, void* stream) {
     zero_status st = check_device(plan);
     if (st != ZERO_OK) return st;
-    if (b < 0 || b >= plan->n_buckets) return fail(ZERO_EINVAL, "zero_reduce_shard: bucket %lld out of range", (long long)b);
-    const int64_t* br = plan->h_bucket + b * kBucketFields;
-    const int64_t base = br[BF_BASE], row = br[BF_ROW], stride = br[BF_STRIDE];
-    if (row == 0) return ZERO_OK;  // empty rows: nothing to read or write, buffers may be NULL
-    if (!d_rows || !d_live || !d_g32) return fail(ZERO_EINVAL, "zero_reduce_shard: NULL pointer");
-    if (!host_aligned16(d_rows) || !host_aligned16(d_g32))
-        return fail(ZERO_EINVAL, "zero_reduce_shard: rows and g32 must be 16-byte aligned");
-    if (row_stride < stride || row_stride % kChunk != 0)
-        return fail(ZERO_EINVAL, "zero_reduce_shard: row_stride %lld must be >= %lld and a multiple of 8",
-                    (long long)row_stride, (long long)stride);
-    const int64_t tile0 = base >> kTileShift;
-    const int64_t n_tile = ((base + row + kTileCols - 1) >> kTileShift) - tile0;
-    const int g = grid_for((n_tile + kReduceTiles - 1) / kReduceTiles);
+    ReduceLaunch L;
+    if ((st = reduce_prepare(plan, b, d_rows, row_stride, d_live, d_g32, d_flag, "zero_reduce_shard", &L)) != ZERO_OK ||
+        L.blocks == 0)
+        return st;
     hipStream_t s = (hipStream_t)stream;
-    const uint16_t* rows = static_cast<const uint16_t*>(d_rows);
     if (plan->dtype == ZERO_BF16)
-        reduce_kernel<ZERO_BF16><<<g, kBlock, 0, s>>>(plan->dev, base, row, tile0, n_tile, rows, row_stride, d_live,
-                                                      d_g32, d_flag);
+        reduce_kernel<ZERO_BF16><<<int(L.blocks), kBlock, 0, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile,
+                                                                  L.rows, L.row_stride, L.live, L.g32, L.flag);
     else
-        reduce_kernel<ZERO_FP16><<<g, kBlock, 0, s>>>(plan->dev, base, row, tile0, n_tile, rows, row_stride, d_live,
-                                                      d_g32, d_flag);
+        reduce_kernel<ZERO_FP16><<<int(L.blocks), kBlock, 0, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile,
+                                                                  L.rows, L.row_stride, L.live, L.g32, L.flag);
     return check_launch("zero_reduce_shard");
 }
 

@@ -195,7 +195,10 @@ __device__ __forceinline__ bool non_finite(float f) { return (__float_as_uint(f)
 // Eight columns of the rank rows: acc = f32(row_0), then acc = acc + f32(row_k) for
 // k = 1..nd-1 (one fp32 round-to-nearest-even addition each, in this order).  Loads of the
 // next kAhead rows are issued ahead of their adds.
-constexpr int kAhead = 8;
+#ifndef ZS_REDUCE_AHEAD
+#define ZS_REDUCE_AHEAD 8
+#endif
+constexpr int kAhead = ZS_REDUCE_AHEAD;
 template <int DT>
 __device__ __forceinline__ void reduce_rows8(const uint16_t* __restrict__ src, int64_t nd, int64_t row_stride,
                                              float (&acc)[8]) {

@@ -147,9 +147,15 @@ class Zero3Schedule:
     so a pass can also be captured into a graph.  At most two layers' parameters exist at a
     time.  `use` callbacks run with the caller's stream current."""
 
-    def __init__(self, st: ShardStep, prefetch: bool = False):
+    def __init__(self, st: ShardStep, prefetch: bool = False, fused: bool = False):
+        """fused=True (one stream only): each backward step is one zero_z3_layer_step launch --
+        the reduce of layer l + 1, the pack of layer l and the gather of layer l - 1 share a
+        launch -- instead of three launches per layer."""
+        if prefetch and fused:
+            raise ValueError("the fused backward runs on one stream (prefetch=False)")
         self.st = st
         self.prefetch = prefetch
+        self.fused = fused
         nb = len(st.buckets)
         infos = [B.zero_plan_param_info(st.plan, i) for i in range(st.n)]
         self.layers = [list(range(int(bk.first_param), int(bk.first_param + bk.n_params))) for bk in st.buckets]
@@ -246,6 +252,9 @@ class Zero3Schedule:
         st = self.st
         out = st.packed if out is None else out
         last = len(self.layers) - 1
+        if self.fused:
+            self._backward_fused(grads_of, rows_of, use, check, out, stream)
+            return
         main = self._main(stream) if self.prefetch else stream
         if self.prefetch:
             self._fork(main)  # the last layer is still in its buffer from the forward pass
@@ -268,3 +277,25 @@ class Zero3Schedule:
             B.zero_reduce_shard(st.plan, lid, rows, stride, st.live, st.g32, st.flag, main)
         if self.prefetch:
             self._join(main)
+
+    def _backward_fused(self, grads_of, rows_of, use, check, out, stream) -> None:
+        """Layers L-1 .. 0; before step l's launch, layer l's parameters are in the scratch (the
+        last layer's since the forward pass) and `use` runs on them; the launch then packs layer
+        l's gradients, gathers layer l - 1 into the scratch and reduces layer l + 1 (packed one
+        step earlier).  A last launch reduces layer 0."""
+        st = self.st
+        last = len(self.layers) - 1
+        for lid in range(last, -2, -1):
+            if lid >= 0 and use is not None:
+                use(lid, self.views[lid])
+            rb = lid + 1 if lid + 1 <= last else -1
+            pb = lid
+            gb = lid - 1 if lid >= 1 else -1
+            rows, stride = rows_of(rb) if rb >= 0 else (None, 0)
+            B.zero_z3_layer_step(st.plan, reduce_b=rb, rows=rows, row_stride=stride, live=st.live, g32=st.g32,
+                                 pack_b=pb, grad_ptrs=grads_of(pb) if pb >= 0 else None,
+                                 packed=st.block(out, pb) if pb >= 0 else None, check=check, gather_b=gb,
+                                 gathered=st.block(st.arena, gb) if gb >= 0 else None,
+                                 param_ptrs=self.tables[gb] if gb >= 0 else None, flag=st.flag, stream=stream)
+            if gb >= 0:
+                self.order.append(gb)
