@@ -683,11 +683,11 @@ def cpu_baseline(w, max_elems: int, device="cuda"):
 
 # ------------------------------------------------------------------- profile summaries --
 
-KERNEL_KEYS = (("adam_prepare_kernel", "adam_prepare"), ("reduce_adam_kernel", "reduce_adam"),
+KERNEL_KEYS = (("probe_adam_streams_kernel", "probe_adam_streams"), ("probe_copy_kernel", "probe_copy"),
+               ("probe_read_kernel", "probe_read"), ("probe_write_kernel", "probe_write"),
+               ("z3_layer_kernel", "z3_layer"), ("adam_prepare_kernel", "adam_prepare"), ("reduce_adam_kernel", "reduce_adam"),
                ("unpack_kernel", "unpack"), ("pack_kernel", "pack"), ("reduce_kernel", "reduce"),
-               ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"),
-               ("adam_streams_kernel", "probe_adam_streams"), ("copy_kernel", "probe_copy"),
-               ("read_kernel", "probe_read"), ("write_kernel", "probe_write"))
+               ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"))
 SHORT_NAMES = tuple(s for _, s in KERNEL_KEYS) + ("pack_check",)
 
 

@@ -21,15 +21,15 @@ __device__ __forceinline__ f32x4 ldf(const float* p) { return *(const ZP_GLOBAL 
 __device__ __forceinline__ void stf(float* p, f32x4 v) { *(ZP_GLOBAL f32x4*)p = v; }
 
 // chunks: 16-byte chunks of the stream; one per thread per iteration of the grid-stride loop
-__global__ __launch_bounds__(kBlock) void read_kernel(const u32x4* __restrict__ src, int64_t chunks,
-                                                      u32x4* __restrict__ sink) {
+__global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4* __restrict__ src, int64_t chunks,
+                                                            u32x4* __restrict__ sink) {
     u32x4 acc = {0u, 0u, 0u, 0u};
     for (int64_t c = blockIdx.x * int64_t(kBlock) + threadIdx.x; c < chunks; c += int64_t(gridDim.x) * kBlock)
         acc ^= ld(src + c);
     if (acc.x == 0x9e3779b9u && acc.y == 0x7f4a7c15u) st(sink, acc);
 }
 
-__global__ __launch_bounds__(kBlock) void write_kernel(u32x4* __restrict__ dst, int64_t chunks) {
+__global__ __launch_bounds__(kBlock) void probe_write_kernel(u32x4* __restrict__ dst, int64_t chunks) {
     for (int64_t c = blockIdx.x * int64_t(kBlock) + threadIdx.x; c < chunks; c += int64_t(gridDim.x) * kBlock) {
         const uint32_t w = uint32_t(c);
         const u32x4 v = {w, w ^ 0x55555555u, w ^ 0xaaaaaaaau, ~w};
@@ -37,16 +37,17 @@ __global__ __launch_bounds__(kBlock) void write_kernel(u32x4* __restrict__ dst, 
     }
 }
 
-__global__ __launch_bounds__(kBlock) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                      int64_t chunks) {
+__global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                            int64_t chunks) {
     for (int64_t c = blockIdx.x * int64_t(kBlock) + threadIdx.x; c < chunks; c += int64_t(gridDim.x) * kBlock)
         st(dst + c, ld(src + c));
 }
 
 // groups: 8-column groups; thread = one group (two 16-byte accesses per fp32 stream)
-__global__ __launch_bounds__(kBlock) void adam_streams_kernel(const float* __restrict__ g, float* __restrict__ p,
-                                                              float* __restrict__ m, float* __restrict__ v,
-                                                              uint16_t* __restrict__ lp, int64_t groups) {
+__global__ __launch_bounds__(kBlock) void probe_adam_streams_kernel(const float* __restrict__ g,
+                                                                    float* __restrict__ p, float* __restrict__ m,
+                                                                    float* __restrict__ v, uint16_t* __restrict__ lp,
+                                                                    int64_t groups) {
     for (int64_t q = blockIdx.x * int64_t(kBlock) + threadIdx.x; q < groups; q += int64_t(gridDim.x) * kBlock) {
         const int64_t x = 8 * q;
         const f32x4 g0 = ldf(g + x), g1 = ldf(g + x + 4);
@@ -78,15 +79,15 @@ zero_status launched() { return hipGetLastError() == hipSuccess ? ZERO_OK : ZERO
 extern "C" zero_status zero_probe_read(const void* d_src, int64_t bytes, void* d_sink, void* stream) {
     if (!d_src || !d_sink || bytes <= 0 || bytes % 16 || !a16(d_src) || !a16(d_sink)) return ZERO_EINVAL;
     const int64_t chunks = bytes / 16;
-    read_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(d_src), chunks,
-                                                                  static_cast<u32x4*>(d_sink));
+    probe_read_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(d_src), chunks,
+                                                                        static_cast<u32x4*>(d_sink));
     return launched();
 }
 
 extern "C" zero_status zero_probe_write(void* d_dst, int64_t bytes, void* stream) {
     if (!d_dst || bytes <= 0 || bytes % 16 || !a16(d_dst)) return ZERO_EINVAL;
     const int64_t chunks = bytes / 16;
-    write_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<u32x4*>(d_dst), chunks);
+    probe_write_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<u32x4*>(d_dst), chunks);
     return launched();
 }
 
@@ -96,8 +97,8 @@ extern "C" zero_status zero_probe_copy(const void* d_src, void* d_dst, int64_t b
     const char* d = static_cast<const char*>(d_dst);
     if (s < d + bytes && d < s + bytes) return ZERO_EINVAL;  // overlapping buffers
     const int64_t chunks = bytes / 16;
-    copy_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(d_src),
-                                                                  static_cast<u32x4*>(d_dst), chunks);
+    probe_copy_kernel<<<grid(chunks), kBlock, 0, (hipStream_t)stream>>>(static_cast<const u32x4*>(d_src),
+                                                                        static_cast<u32x4*>(d_dst), chunks);
     return launched();
 }
 
@@ -106,6 +107,6 @@ extern "C" zero_status zero_probe_adam_streams(const float* d_g, float* d_p, flo
     if (!d_g || !d_p || !d_m || !d_v || !d_lp || n <= 0 || n % 8) return ZERO_EINVAL;
     if (!a16(d_g) || !a16(d_p) || !a16(d_m) || !a16(d_v) || !a16(d_lp)) return ZERO_EINVAL;
     const int64_t groups = n / 8;
-    adam_streams_kernel<<<grid(groups), kBlock, 0, (hipStream_t)stream>>>(d_g, d_p, d_m, d_v, d_lp, groups);
+    probe_adam_streams_kernel<<<grid(groups), kBlock, 0, (hipStream_t)stream>>>(d_g, d_p, d_m, d_v, d_lp, groups);
     return launched();
 }
