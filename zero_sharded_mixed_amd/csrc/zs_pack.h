@@ -12,6 +12,7 @@ namespace zs {
 #endif
 constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
 
+
 // The input check of the checked pack: true if one of the eight 16-bit values is inf or NaN
 // or larger in magnitude than 2^126 / Nd (below it no fp32 sum of Nd values overflows).  For
 // bf16 and fp16 alike, finite magnitudes order as their bit patterns with the sign cleared, and
@@ -29,6 +30,30 @@ __device__ __forceinline__ bool out_of_range8(const uint4& v, uint32_t limit) {
 // Eight elements of one row of parameter m, starting at element e of its flat gradient:
 // one unaligned 16-byte load when all eight are gradient elements, else element by element
 // with +0 for the padding (e >= numel).
+// Eight elements starting at element e of a 16-byte aligned buffer, from the two aligned
+// granules that hold them (never a granule that holds none of the eight): the d = e mod 8
+// element shift is a selection of 32-bit words by d/2 and a 2-byte funnel shift when d is odd.
+__device__ __forceinline__ uint4 funnel8(const uint4& a, const uint4& b, int d) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const int h = d >> 1;
+    const uint32_t sh = (d & 1) ? 2u : 0u;
+    uint32_t lo[5];
+#pragma unroll
+    for (int t = 0; t < 5; ++t) {  // lo[t] = w[h + t] (h in 0..3, h + t <= 7)
+        const uint32_t c0 = w[t], c1 = w[t + 1 < 8 ? t + 1 : 7], c2 = w[t + 2 < 8 ? t + 2 : 7],
+                       c3 = w[t + 3 < 8 ? t + 3 : 7];
+        lo[t] = h == 0 ? c0 : h == 1 ? c1 : h == 2 ? c2 : c3;
+    }
+    return make_uint4(__builtin_amdgcn_alignbyte(lo[1], lo[0], sh), __builtin_amdgcn_alignbyte(lo[2], lo[1], sh),
+                      __builtin_amdgcn_alignbyte(lo[3], lo[2], sh), __builtin_amdgcn_alignbyte(lo[4], lo[3], sh));
+}
+__device__ __forceinline__ uint4 load8_two(const uint16_t* __restrict__ base, int64_t e) {
+    const int64_t q = e >> 3;
+    const int d = int(e & 7);
+    const uint4 a = load16(base + 8 * q);
+    if (d == 0) return a;
+    return funnel8(a, load16(base + 8 * q + 8), d);
+}
 __device__ __forceinline__ uint4 row_chunk(const uint16_t* g, int64_t e, int64_t numel) {
     if (e + kChunk <= numel) return load16_any(g + e);
     const ZS_GLOBAL uint16_t* gg = gptr(g);
@@ -313,10 +338,12 @@ __device__ __forceinline__ uint4 merge_split(const uint4& a, const uint4& b, int
 
 // One chunk of parameter fields (numel, s, column of the slice in the rows, 1/s, chunk base).
 // Element e0..e0+7 of the parameter: row k = e0 / s, column j0 = e0 mod s.  A chunk inside one
-// row is one 16-byte load at the row's alignment; a chunk crossing into the next row (s >= 8)
-// is two loads and a merge (a crossing chunk is never in the last row, so both loads stay
-// inside the block); the tail of a parameter and rows shorter than 8 go element by element.
-// The store is one 16-byte store whatever the output's 2-byte alignment.
+// row is read from the aligned granules of the (16-byte aligned) gathered block that hold it
+// (load8_two; measured on MI355X 1% faster here than one unaligned load, and 6% faster than
+// taking the second granule from the next lane by a DPP shift); a chunk crossing into the next
+// row (s >= 8) is two such reads and a merge (a crossing chunk is never in the last row, so
+// both stay inside the block); the tail of a parameter and rows shorter than 8 go element by
+// element.  The store is one 16-byte store whatever the output's 2-byte alignment.
 __device__ __forceinline__ void unpack_chunk(int64_t u, int64_t ucb, int64_t numel, int64_t s, int64_t col,
                                              double inv_s, int64_t b_stride, const uint16_t* __restrict__ gathered,
                                              uint16_t* out) {
@@ -327,12 +354,12 @@ __device__ __forceinline__ void unpack_chunk(int64_t u, int64_t ucb, int64_t num
     if (j0 < 0) { --k; j0 += s; } else if (j0 >= s) { ++k; j0 -= s; }
     if (e0 + kChunk <= numel) {
         if (j0 + kChunk <= s) {
-            store16_any(out + e0, load16_any(gathered + k * b_stride + col + j0));
+            store16_any(out + e0, load8_two(gathered, k * b_stride + col + j0));
             return;
         }
         if (s >= kChunk) {
-            const uint4 a = load16_any(gathered + k * b_stride + col + j0);
-            const uint4 b = load16_any(gathered + (k + 1) * b_stride + col);
+            const uint4 a = load8_two(gathered, k * b_stride + col + j0);
+            const uint4 b = load8_two(gathered, (k + 1) * b_stride + col);
             store16_any(out + e0, merge_split(a, b, int(s - j0)));
             return;
         }
@@ -388,7 +415,7 @@ __device__ __forceinline__ void unpack_body(const DevPlan& P, int64_t b_base, in
                     int64_t j0 = js + d, k = ks;
                     if (j0 >= s) { j0 -= s; ++k; }
                     if (e0 + kChunk <= numel && j0 + kChunk <= s)
-                        store16_any(out + e0, load16_any(gathered + k * b_stride + col + j0));
+                        store16_any(out + e0, load8_two(gathered, k * b_stride + col + j0));
                     else
                         unpack_chunk(ua + t * kUTileChunks + threadIdx.x, ucb, numel, s, col, inv_s, b_stride,
                                      gathered, out);
