@@ -120,7 +120,8 @@ constexpr int kStageMax = ZS_STAGE_MAX;
 //    length (the list entry carries the parameter) and the rows of a block share it.
 // Measured on MI355X: one row per block, four, or tiles varying fastest, lose 2-20% on the
 // whole-tile lists; a fixed grid that prefetches the next item loses 10-40% against this
-// one-block-per-item grid; 4, 16 or 32 rows per mixed block are slower than 8.
+// one-block-per-item grid; 4 rows per mixed block are 1% slower than 8 on the ragged list,
+// 16 rows 4-38% slower (the run's 16 loads in flight cost registers, hence occupancy).
 // tiles: the bucket's n_whole whole tiles, then its n_mixed mixed tiles (plan tables).
 #ifndef ZS_MIX_ROWS
 #define ZS_MIX_ROWS 8
@@ -129,6 +130,7 @@ constexpr int kStageMax = ZS_STAGE_MAX;
 #define ZS_WHOLE_ROWS 2
 #endif
 constexpr int kMixRows = ZS_MIX_ROWS;        // rows per block of a mixed tile
+static_assert(kMixRows >= 1 && kMixRows < 32, "a run's rows are a 32-bit mask");
 constexpr int kWholeRows = ZS_WHOLE_ROWS;    // rows per block of a whole tile
 
 // The fields a whole-tile work item needs: its rows, its columns' parameter and that
@@ -189,6 +191,8 @@ struct MixMeta {
     int32_t run0;   // index of that run in the tile's list (exclusive scan of the run counts)
 };
 
+// The kMixRows rows of one run: every row's load is issued before the first store, so that a
+// thread waits for memory once per run rather than once per row.
 template <bool CHECK>
 __device__ __forceinline__ void pack_run(const MixMeta& m, int64_t mnum, int64_t k0, int64_t k1,
                                          uint16_t* __restrict__ packed, int64_t b_base, int64_t b_stride,
@@ -196,25 +200,39 @@ __device__ __forceinline__ void pack_run(const MixMeta& m, int64_t mnum, int64_t
     const int64_t s = m.s;
     const int64_t j = (s >= kChunk && 8 * mnum + kChunk > s) ? s - kChunk : 8 * mnum;  // first element of the run
     const int len = int(s - j < kChunk ? s - j : kChunk);
-    const uint16_t* src = m.g + j;
+    const uint16_t* __restrict__ src = m.g + j;
     const int64_t lim = m.numel - j;  // element e of the run exists iff k * s + e < lim
-    uint16_t* dst = packed + (m.off + j - b_base);
-    for (int64_t k = k0; k < k1; ++k) {
-        const int64_t e = k * s;
-        if (len == kChunk && e + kChunk <= lim) {
-            const uint4 v = load16_any(src + e);
-            if constexpr (CHECK) bad |= out_of_range8(v, limit);
-            store16_any(dst + k * b_stride, v);
-        } else {
-            ZS_GLOBAL uint16_t* d = gptr(dst + k * b_stride);
-            uint16_t h[8];
+    uint16_t* __restrict__ dst = packed + (m.off + j - b_base);
+    uint4 v[kMixRows];
+    unsigned fast = 0;  // bit u: row k0 + u is one 16-byte load and store
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                h[t] = (t < len && e + t < lim) ? gptr(src)[e + t] : uint16_t(0);
-                if (t < len) d[t] = h[t];
-            }
-            if constexpr (CHECK) bad |= out_of_range8(pack8(h), limit);
+    for (int u = 0; u < kMixRows; ++u) {
+        const int64_t k = k0 + u;
+        if (k < k1 && len == kChunk && k * s + kChunk <= lim) {
+            v[u] = load16_any(src + k * s);
+            fast |= 1u << u;
         }
+    }
+#pragma unroll
+    for (int u = 0; u < kMixRows; ++u) {
+        if (fast & (1u << u)) {
+            if constexpr (CHECK) bad |= out_of_range8(v[u], limit);
+            store16_any(dst + (k0 + u) * b_stride, v[u]);
+        }
+    }
+    if (fast == (1u << (k1 - k0)) - 1u) return;
+    // runs shorter than 8 or reaching into the padding: element by element, +0 past numel
+    for (int64_t k = k0; k < k1; ++k) {
+        if (fast & (1u << (k - k0))) continue;
+        const int64_t e = k * s;
+        ZS_GLOBAL uint16_t* d = gptr(dst + k * b_stride);
+        uint16_t h[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            h[t] = (t < len && e + t < lim) ? gptr(src)[e + t] : uint16_t(0);
+            if (t < len) d[t] = h[t];
+        }
+        if constexpr (CHECK) bad |= out_of_range8(pack8(h), limit);
     }
 }
 
@@ -304,20 +322,21 @@ __device__ __forceinline__ void pack_body(const DevPlan& P, PackShared& sh, int6
     const int64_t n_mrg = (P.nd + kMixRows - 1) / kMixRows;
     const int64_t n_work = n_wwork + n_mixed * n_mrg;
     bool bad = false;
-    // the mixed items (several rows each, heavier) first, so that they do not form the tail
+    // the mixed items (several rows each, heavier) first, so that they do not form the tail;
+    // two loops, so that a block with whole items only sets up nothing of the mixed ones
     const int64_t n_mwork = n_work - n_wwork;
-    for (int64_t w = vbid; w < n_work; w += vgrid) {
-        if (w >= n_mwork) {
-            const WholeItem it = whole_item(P, tiles, grads, w - n_mwork, n_wrg, n_whole);
-            if (!it.g) continue;  // no gradient this step
-            uint4 v[kWholeRows];
-            whole_loads<CHECK>(P, it, v, limit, bad);
-            whole_stores(P, it, v, packed, b_base, b_stride);
-            continue;
-        }
+    int64_t w = vbid;
+    for (; w < n_mwork; w += vgrid) {
         const int64_t kg = w / n_mixed;
         pack_mixed_item<CHECK>(P, sh.sm, &sh.total, b_base, b_row, b_stride, tiles, n_whole + (w - kg * n_mixed), kg,
                                grads, packed, limit, bad);
+    }
+    for (; w < n_work; w += vgrid) {
+        const WholeItem it = whole_item(P, tiles, grads, w - n_mwork, n_wrg, n_whole);
+        if (!it.g) continue;  // no gradient this step
+        uint4 v[kWholeRows];
+        whole_loads<CHECK>(P, it, v, limit, bad);
+        whole_stores(P, it, v, packed, b_base, b_stride);
     }
     if constexpr (CHECK) flag_wave(bad, flag);
 }
