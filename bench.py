@@ -43,6 +43,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "shard step GB/s & elem/s (pack+reduce+Adam) vs HBM peak, 1 MI355X"
 HEADLINE = 4
 OTHERS = (2, 3, 5)
+ZERO3_BATCH = 2   # consecutive layers per launch in the ZeRO-3 leg
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 WORKLOAD_IDS = {1: "mlp-nd8-r3", 2: "gpt2-1.5b-nd8-r0", 3: "llama-7b-nd8-r5", 4: "paper-7.5b-nd64-r63",
                 5: "ragged-10k-nd1024-r517"}
@@ -308,17 +309,19 @@ def run_graph(w, ctx, steps, warmup):
     return ms
 
 
-def run_zero3(w, ctx, steps, warmup, device, graph=True, prefetch=False):
+def run_zero3(w, ctx, steps, warmup, device, graph=True, prefetch=False, batch=ZERO3_BATCH, sweep=()):
     """ZeRO-3's step on the same list with one bucket per layer (workloads.layer_groups): the
     forward pass gathers every layer's parameters (unpack into a scratch buffer), the backward
     pass gathers all but the last layer again and reduce-scatters each layer's gradients (pack
     + reduce) right after it, then Adam writes this rank's 16-bit shard.  Full emulation: every
     virtual rank's gradients are packed for the per-layer buckets beforehand; this rank's are
     re-packed inside each timed step, into the rows the reduce reads.  All on one stream, each
-    backward step one zero_z3_layer_step launch; `separate_launches` times the same step with a
-    launch per piece (and `speedup` = its time / the fused schedule's); with prefetch=True also
-    with the gathers on a second stream into two scratch buffers.  With graph=True each step is
-    also captured into a HIP graph and replayed."""
+    launch (zero_z3_step) handles `batch` consecutive layers: the forward gathers them, a
+    backward launch packs them, gathers the batch before and reduces the batch after; `batch_1`
+    times the same with one layer per launch, `separate_launches` with a launch per piece
+    (`speedup` = their time / the main schedule's); `sweep` lists other batches to time; with
+    prefetch=True also with the gathers on a second stream into two scratch buffers.  With graph=True each step is also
+    captured into a HIP graph and replayed."""
     import workloads as W
 
     st2, live = ctx.st, ctx.live
@@ -402,18 +405,35 @@ def run_zero3(w, ctx, steps, warmup, device, graph=True, prefetch=False):
             del g
         return res
 
-    z3 = Z.Zero3Schedule(z, fused=True)
+    z3 = Z.Zero3Schedule(z, fused=True, batch=batch)
     torch.cuda.synchronize()
     log(f"[bench] zero3: {len(z.buckets)} layer buckets, scratch {z3.scratch.numel()} elements "
         f"({time.time() - t0:.1f}s)")
     out = measure(z3)
-    out["schedule"] = "one stream; each backward step one launch (reduce l+1, pack l, gather l-1)"
+    out["schedule"] = (f"one stream; {batch} consecutive layers per launch; forward: gather; backward: reduce "
+                       "the batch after, pack this batch, gather the batch before")
+    out["batch"] = batch
     del z3
-    z3 = Z.Zero3Schedule(z)  # the same step with three launches per backward layer
+    if batch != 1:  # the same with one layer per launch
+        z3 = Z.Zero3Schedule(z, fused=True)
+        one = measure(z3)
+        one["speedup"] = round(one["ms_per_step"] / out["ms_per_step"], 3)
+        out["batch_1"] = one
+        del z3
+    z3 = Z.Zero3Schedule(z)  # one launch per gather, pack and reduce
     sep = measure(z3)
     sep["speedup"] = round(sep["ms_per_step"] / out["ms_per_step"], 3)
     out["separate_launches"] = sep
     del z3
+    if sweep:
+        out["batch_sweep"] = {}
+        for k in sweep:
+            z3 = Z.Zero3Schedule(z, fused=True, batch=k)
+            r = measure(z3)
+            out["batch_sweep"][str(k)] = {"ms_per_step": r["ms_per_step"], "GBs": r["GBs"],
+                                                 "forward_ms": r["phases"]["forward"]["ms"],
+                                                 "backward_ms": r["phases"]["backward"]["ms"], "scratch_elems": r["scratch_elems"]}
+            del z3
     if prefetch:  # the gathers on a second stream into two scratch buffers
         z3 = Z.Zero3Schedule(z, prefetch=True)
         pf = measure(z3)
@@ -541,7 +561,8 @@ def measure_workload(w, args, device, headline: bool):
                         "speedup": round(ms / gms, 3)}
     if w.emulation == "full" and not args.no_zero3 and not headline:
         res["zero3"] = run_zero3(w, ctx, args.steps, args.warmup, device, graph=not args.no_graph,
-                                 prefetch=args.zero3_prefetch)
+                                 prefetch=args.zero3_prefetch, batch=args.zero3_batch,
+                                 sweep=[int(x) for x in args.zero3_sweep.split(",") if x])
     del ctx
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -558,6 +579,9 @@ def run_children(configs, args):
         for flag in ("no_graph", "no_zero3", "zero3_prefetch"):
             if getattr(args, flag):
                 cmd.append("--" + flag.replace("_", "-"))
+        cmd += ["--zero3-batch", str(args.zero3_batch)]
+        if args.zero3_sweep:
+            cmd += ["--zero3-sweep", args.zero3_sweep]
         log(f"[bench] workload {WORKLOAD_IDS[c]} (child process) ...")
         t0 = time.time()
         try:
@@ -840,6 +864,9 @@ def main():
     ap.add_argument("--no-zero3", action="store_true", help="skip the ZeRO-3 (one bucket per layer) leg")
     ap.add_argument("--zero3-prefetch", action="store_true",
                     help="also time ZeRO-3 with the gathers on a second stream (slower without model compute)")
+    ap.add_argument("--zero3-batch", type=int, default=ZERO3_BATCH,
+                    help="consecutive layers per launch in the ZeRO-3 leg (1 = one layer per launch)")
+    ap.add_argument("--zero3-sweep", default="", help="comma-separated other batches to time")
     ap.add_argument("--no-graph", action="store_true", help="skip the leg that replays the step as a HIP graph")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="reduce rocprofv3 CSVs under DIR (trace/, FETCH_SIZE/, WRITE_SIZE/) to a text summary "

@@ -399,6 +399,41 @@ zero_status zero_z3_layer_step(const zero_plan* plan, int64_t reduce_b, const vo
                                void* d_packed, int32_t check, int64_t gather_b, const void* d_gathered,
                                void* const* d_param_ptrs, int32_t* d_flag, void* stream);
 
+/* Most buckets in one piece of a zero_z3_step call. */
+#define ZERO_Z3_MAX_BUCKETS 4
+
+/* The pieces of one zero_z3_step launch: up to ZERO_Z3_MAX_BUCKETS consecutive buckets of each
+ * kind.  A count of 0 leaves the kind out (its fields are not read).  Host struct, read during
+ * the call; the pointers in it are device pointers. */
+typedef struct zero_z3_pieces {
+    int64_t reduce_b0, reduce_n;                  /* reduce buckets [reduce_b0, reduce_b0 + reduce_n) */
+    const void* rows[ZERO_Z3_MAX_BUCKETS];        /* rows of bucket reduce_b0 + j (zero_reduce_shard's d_rows) */
+    int64_t row_stride[ZERO_Z3_MAX_BUCKETS];      /* and its row stride */
+    const uint8_t* live;                          /* as zero_reduce_shard */
+    float* g32;                                   /* as zero_reduce_shard */
+    int64_t pack_b0, pack_n;                      /* pack buckets [pack_b0, pack_b0 + pack_n) */
+    const void* const* grad_ptrs;                 /* as zero_pack_bucket */
+    void* packed[ZERO_Z3_MAX_BUCKETS];            /* packed block of bucket pack_b0 + j */
+    int32_t check;                                /* != 0: the checked pack (zero_pack_bucket_check) */
+    int64_t gather_b0, gather_n;                  /* unpack buckets [gather_b0, gather_b0 + gather_n) */
+    const void* gathered[ZERO_Z3_MAX_BUCKETS];    /* all-gather block of bucket gather_b0 + j */
+    void* const* param_ptrs;                      /* as zero_unpack */
+    int32_t* flag;                                /* overflow flag of the reduces and the checked packs */
+} zero_z3_pieces;
+
+/* zero_z3_layer_step over ranges of buckets [Z3: the forward pass gathers layers in order and
+ * the backward pass goes back through them, reduce-scattering each layer's gradients once its
+ * backward has run; consecutive layers can be handled together]: every bucket of every piece
+ * computes exactly what its own entry point computes (zero_reduce_shard, zero_pack_bucket or
+ * zero_pack_bucket_check, zero_unpack) with that bucket's pointers from *pieces; all buckets
+ * share one grid and run concurrently, so no bucket's work may read or write what another's
+ * writes.  With one bucket per layer and k layers per step, a backward step packs layers
+ * [l, l + k), gathers [l - k, l) and reduces [l + k, l + 2k); a forward step gathers k layers.
+ * Errors: ZERO_EINVAL for NULL pieces, a count outside 0 .. ZERO_Z3_MAX_BUCKETS, a range
+ * outside [0, n_buckets), or whatever a bucket's own entry point rejects (nothing is launched
+ * then). */
+zero_status zero_z3_step(const zero_plan* plan, const zero_z3_pieces* pieces, void* stream);
+
 /* ------------------------------------------------------- dynamic loss scaling ------ */
 
 /* Write the host configuration *cfg (every field, good_steps and overflows included) to the

@@ -3,6 +3,7 @@ raw pointer is checked against the plan's sizes before anything is launched (a m
 buffer would otherwise become an out-of-bounds device access).  Stand-in plan and tensor
 objects carry exactly the attributes the checks read, so no device is needed; the GPU tests
 drive the same checks through the real entry points."""
+import ctypes
 import os
 import subprocess
 
@@ -21,6 +22,7 @@ class FakePlan:
     n_buckets = 1
     numels = np.array([1000, 37, 5000], dtype=np.int64)
     row_stride = [760]
+    block_offset = [0]
     shard_numel = 760
     arena_numel = 8 * 760
     block_elems = B.Plan.block_elems
@@ -135,3 +137,45 @@ int main() {
     for w in (str((1 << 23) + 1), str(1 << 31), str(1 << 40), str(65535 * 8388608)):
         assert int(got[w]) == 1 << 23  # 2^23 blocks x 256 threads = 2^31 work-items < 2^32
     assert got["cap4"] == "4"
+
+
+def test_z3_step_pieces_checked():
+    """Every bucket of every piece is checked against its own block size; piece lengths above
+    the maximum and a row-stride list of the wrong length are refused."""
+    ok = fake_table([FakeTensor(x) for x in P.numels])
+    with pytest.raises(ValueError, match="at least"):
+        B.zero_z3_step(P, gather_b0=0, gathered=[FakeTensor(P.block_elems(0) - 1)], param_ptrs=ok)
+    with pytest.raises(ValueError, match="entry 2"):
+        B.zero_z3_step(P, gather_b0=0, gathered=[FakeTensor(P.block_elems(0))],
+                       param_ptrs=fake_table([FakeTensor(1000), None, FakeTensor(4999)]))
+    with pytest.raises(ValueError, match="at least"):
+        B.zero_z3_step(P, pack_b0=0, grad_ptrs=ok, packed=[FakeTensor(P.block_elems(0) - 8)])
+    with pytest.raises(ValueError, match="at least"):  # rows of a reduce at a stride above L_b
+        B.zero_z3_step(P, reduce_b0=0, rows=[FakeTensor(P.rows_elems(0, 800) - 1)], row_strides=[800],
+                       live=FakeTensor(3, torch.uint8), g32=FakeTensor(P.shard_numel, torch.float32))
+    with pytest.raises(ValueError, match="row strides"):
+        B.zero_z3_step(P, reduce_b0=0, rows=[FakeTensor(P.rows_elems(0, 800))], row_strides=[])
+    with pytest.raises(ValueError, match="at most"):
+        B.zero_z3_step(P, gather_b0=0, gathered=[FakeTensor(1)] * (B.Z3_MAX_BUCKETS + 1), param_ptrs=ok)
+
+
+def test_z3_pieces_layout_matches_the_header():
+    """The ctypes mirror of zero_z3_pieces has the C struct's size and field offsets (the host
+    compiler lays out the header's struct; x86-64 and the device share the layout rules)."""
+    inc = os.path.join(ROOT, "include")
+    fields = [f for f, _ in B.zero_z3_pieces._fields_]
+    prog = "#include <cstdio>\n#include <cstddef>\n#include \"zero_shard.h\"\nint main() {\n"
+    prog += '    std::printf("size %zu\\n", sizeof(zero_z3_pieces));\n'
+    prog += "".join(f'    std::printf("{f} %zu\\n", offsetof(zero_z3_pieces, {f}));\n' for f in fields)
+    prog += '    std::printf("max %d\\n", ZERO_Z3_MAX_BUCKETS);\n}\n'
+    exe = os.path.join(os.environ.get("TMPDIR", "/tmp"), f"zs_z3_layout_{os.getpid()}")
+    subprocess.run(["g++", "-std=c++17", "-I", inc, "-x", "c++", "-", "-o", exe], input=prog, text=True, check=True)
+    try:
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    finally:
+        os.remove(exe)
+    got = {k: int(v) for k, v in (line.split() for line in out if line)}
+    assert got["max"] == B.Z3_MAX_BUCKETS
+    assert got["size"] == ctypes.sizeof(B.zero_z3_pieces)
+    for f in fields:
+        assert got[f] == getattr(B.zero_z3_pieces, f).offset, f

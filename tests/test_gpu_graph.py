@@ -116,7 +116,7 @@ def _release():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused"])
+@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused", "fused-batch2"])
 @pytest.mark.parametrize("nd,rank", [(8, 3), (64, 17)])
 def test_captured_zero3_step_replays_like_eager_steps(nd, rank, mode):
     prefetch = mode == "prefetch"
@@ -146,7 +146,7 @@ def test_captured_zero3_step_replays_like_eager_steps(nd, rank, mode):
     gptrs = Z.ptr_table([to_dev16(random_bits(rng, x) & np.uint16(0xBBFF)) if l else None
                          for x, l in zip(numels, live)])
     rows = [to_dev16(random_bits(rng, nd * int(bk.row_stride)) & np.uint16(0xBBFF)) for bk in st.buckets]
-    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused")
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode.startswith("fused"), batch=2 if "batch" in mode else 1)
     out = torch.zeros_like(st.packed)
 
     def rows_of(lid):
@@ -165,6 +165,8 @@ def test_captured_zero3_step_replays_like_eager_steps(nd, rank, mode):
         step()
         torch.cuda.synchronize()
         eager.append([t.clone() for t in bufs])
+    # one layer per launch, or batches [0, 1], [2, 3], [4]: either way the last layer (batch)
+    # is not gathered twice
     assert z3.order == [0, 1, 2, 3, 4, 3, 2, 1, 0] * 3
     for t, s0 in zip(bufs, start):
         t.copy_(s0)

@@ -251,7 +251,8 @@ def test_random_zero3_schedule(seed):
     dtype = BF16 if rng.random() < 0.5 else FP16
     mode = ("one-stream", "prefetch", "fused")[int(rng.integers(0, 3))]
     prefetch = mode == "prefetch"
-    say(f"zero3 sweep seed={seed} nd={nd} rank={rank} layers={n_layers} n={len(numels)} {mode}")
+    batch = int(rng.integers(1, Z.Z3_MAX_BUCKETS + 1)) if mode == "fused" else 1
+    say(f"zero3 sweep seed={seed} nd={nd} rank={rank} layers={n_layers} n={len(numels)} {mode} batch={batch}")
     st = Z.ShardStep(numels, nd, rank, 0, dtype, groups=groups)
     pl = oracle.plan(numels, nd, rank, 0, np.array(groups, np.int32))
     assert pl.n_buckets == n_layers
@@ -268,7 +269,7 @@ def test_random_zero3_schedule(seed):
     steps = np.zeros(len(numels), np.int32)
     live = (rng.random(len(numels)) > 0.2).astype(np.uint8)
     st.live.copy_(torch.from_numpy(live))
-    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused")
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused", batch=batch)
 
     def check_gather(lid, params):
         outs = [np.zeros(x, np.uint16) for x in numels]
@@ -294,7 +295,8 @@ def test_random_zero3_schedule(seed):
     z3.forward(check_gather)
     z3.backward(lambda lid: gptrs, lambda lid: (rdev[lid], int(pl.buckets[lid, oracle.B_STRIDE])), check_gather,
                 out=out)
-    assert z3.order == list(range(n_layers)) + list(range(n_layers - 2, -1, -1))
+    last = z3.batches[-1][1] - z3.batches[-1][0]  # the last batch is not gathered twice
+    assert z3.order == list(range(n_layers)) + list(range(n_layers - last - 1, -1, -1))
     torch.cuda.synchronize()
     got_out = to_np16(out)
     for b in range(pl.n_buckets):

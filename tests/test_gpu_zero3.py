@@ -16,6 +16,11 @@ pytestmark = pytest.mark.gpu
 BF16, FP16 = Z.ZERO_BF16, Z.ZERO_FP16
 
 
+def batch_of(mode):
+    """Layers per forward gather launch of a schedule mode ("fused-batch3" -> 3)."""
+    return int(mode.split("batch")[1]) if "batch" in mode else 1
+
+
 def layered_model(n_layers, d, vocab):
     """Embedding, then blocks of [w1 (d x 4d), b1 (4d), w2 (4d x d), b2 (d), ln w (d), ln b (d)],
     then a final norm; returns numels and the layer (group) of each parameter."""
@@ -50,7 +55,7 @@ def test_grouped_plan_tables(nd, cap, seed):
         assert np.all(members == members[0])  # a bucket never spans two runs of ids
 
 
-@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused"])
+@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused", "fused-batch3"])
 @pytest.mark.parametrize("nd,rank,dtype", [(8, 3, BF16), (64, 17, FP16)])
 def test_zero3_step_matches_oracle(nd, rank, dtype, mode):
     prefetch = mode == "prefetch"
@@ -76,7 +81,7 @@ def test_zero3_step_matches_oracle(nd, rank, dtype, mode):
     live = np.ones(len(numels), np.uint8)
     live[[3, 4]] = 0  # two parameters of layer 1 without a gradient (the layer-drop mapping)
     st.live.copy_(torch.from_numpy(live))
-    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode == "fused")
+    z3 = Z.Zero3Schedule(st, prefetch=prefetch, fused=mode.startswith("fused"), batch=batch_of(mode))
 
     def check_gather(lid, params):
         outs = [np.zeros(x, np.uint16) for x in numels]
@@ -96,7 +101,8 @@ def test_zero3_step_matches_oracle(nd, rank, dtype, mode):
     st.g32.fill_(-3.0)
     z3.forward(check_gather)
     z3.backward(lambda lid: gdev, lambda lid: (rdev[lid], int(pl.buckets[lid, oracle.B_STRIDE])), check_gather)
-    assert z3.order == [0, 1, 2, 3, 4, 3, 2, 1, 0]  # the last layer is not gathered twice
+    # the last layer (the last batch) is not gathered twice
+    assert z3.order == {1: [0, 1, 2, 3, 4, 3, 2, 1, 0], 3: [0, 1, 2, 3, 4, 2, 1, 0]}[batch_of(mode)]
     g32 = np.full(S, -3.0, np.float32)
     for b in range(pl.n_buckets):
         oracle.reduce_bucket(pl, b, rows[b], dtype, live, g32)
@@ -117,15 +123,15 @@ def test_zero3_step_matches_oracle(nd, rank, dtype, mode):
     # model states at stage 3 against the accounting of the ZeRO summary (16 Psi / Nd)
     psi = float(pl.params[:, oracle.P_PADDED].sum())
     assert Z.zero_plan_model_state_bytes(st.plan, 3) == pytest.approx(16 * psi / nd)
-    # at most one layer's full parameters at a time (two with prefetch): each scratch buffer
-    # holds the largest layer
+    # at most one layer's full parameters at a time (two with prefetch, k with batches of k
+    # gathers): each scratch slot holds the largest layer
     biggest = max(sum(numels[i] for i in z3.layers[b]) for b in range(pl.n_buckets))
     assert biggest <= z3.buffer_numel < biggest + 8 * 8
-    assert z3.scratch.numel() == (2 if prefetch else 1) * z3.buffer_numel
+    assert z3.scratch.numel() == (2 if prefetch else batch_of(mode)) * z3.buffer_numel
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused"])
+@pytest.mark.parametrize("mode", ["one-stream", "prefetch", "fused", "fused-batch2"])
 def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(mode):
     prefetch = mode == "prefetch"
     """The GPT-2 1.5B-shaped list at Nd = 8 with one bucket per layer, as bench.py's ZeRO-3 leg
@@ -179,7 +185,7 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(mode):
     hp = (w.lr, w.betas[0], w.betas[1], w.eps, w.grad_scale)
     A.adam(*hp)
     # ZeRO-3
-    z3 = Z.Zero3Schedule(G, prefetch=prefetch, fused=mode == "fused")
+    z3 = Z.Zero3Schedule(G, prefetch=prefetch, fused=mode.startswith("fused"), batch=batch_of(mode))
 
     def restored(lid, params):
         for i, view in zip(z3.layers[lid], params):
@@ -192,7 +198,9 @@ def test_zero3_fullsize_gpt2_matches_zero2_and_oracle(mode):
     G.adam(*hp)
     torch.cuda.synchronize()
     assert int(A.flag.item()) == int(G.flag.item()) == 0
-    assert z3.order == list(range(len(G.buckets))) + list(range(len(G.buckets) - 2, -1, -1))
+    nb = len(G.buckets)
+    last = z3.batches[-1][1] - z3.batches[-1][0]
+    assert z3.order == list(range(nb)) + list(range(nb - last - 1, -1, -1))
     assert torch.equal(A.steps, G.steps)
     for i in range(A.n):
         ia, ig = Z.zero_plan_param_info(A.plan, i), Z.zero_plan_param_info(G.plan, i)
@@ -234,3 +242,114 @@ def test_z3_layer_step_arguments():
     assert e.value.status == Z.ZERO_EINVAL
     torch.cuda.synchronize()
     assert int(st.flag.item()) == 0 and torch.all(st.packed == 0)
+
+
+@pytest.mark.parametrize("nd,rank,dtype,check", [(8, 3, BF16, False), (64, 17, FP16, True), (3, 0, BF16, True)])
+def test_z3_step_ranges_match_single_buckets_and_oracle(nd, rank, dtype, check):
+    """zero_z3_step with ranges of buckets in each piece writes exactly what the per-bucket
+    entry points write: reduce of buckets [0, 3), pack of [3, 6) (checked or not), unpack of
+    [6, 8) -- against zero_reduce_shard, zero_pack_bucket(_check) and zero_unpack bucket by
+    bucket, and the unpacked parameters and the reduce against the oracle.  The model has empty
+    and odd-sized parameters; the unpack destinations are 2-byte misaligned; the receive rows
+    have a stride above L_b."""
+    rng = np.random.default_rng(nd * 10 + rank)
+    n_layers = 8
+    numels, groups = [], []
+    for layer in range(n_layers):
+        for _ in range(int(rng.integers(1, 6))):
+            numels.append(int(rng.choice([0, 1, 7, 9, 100, 1000, 4099, 30000])))
+            groups.append(layer)
+    say(f"z3_step ranges nd={nd} params={len(numels)} check={check}")
+    pl = oracle.plan(numels, nd, rank, 0, np.array(groups, np.int32))
+    assert pl.n_buckets == n_layers
+    live = np.ones(len(numels), np.uint8)
+    live[rng.random(len(numels)) < 0.2] = 0
+    grads = [random_bits(rng, x) & np.uint16(0xBBFF) for x in numels]
+    gdev = Z.ptr_table([to_dev16(g) if l else None for g, l in zip(grads, live)])
+    arena = random_bits(rng, nd * pl.shard_len)
+    rows = [random_bits(rng, nd * (int(pl.buckets[b, oracle.B_STRIDE]) + 16)).reshape(nd, -1) & np.uint16(0xBBFF)
+            for b in range(n_layers)]
+    rdev = [to_dev16(r.reshape(-1)) for r in rows]
+    strides = [int(pl.buckets[b, oracle.B_STRIDE]) + 16 for b in range(n_layers)]
+    outs = {}
+    for mode in ("ranges", "single"):
+        st = Z.ShardStep(numels, nd, rank, 0, dtype, groups=groups)
+        st.live.copy_(torch.from_numpy(live))
+        st.arena.copy_(to_dev16(arena))
+        st.packed.fill_(0x0F0F)
+        st.g32.fill_(-7.0)
+        st.flag.zero_()
+        bufs = [torch.full((x + 2,), 0x1111, dtype=torch.int16, device=DEV) for x in numels]
+        ptrs = Z.ptr_table([t[1:1 + x] for t, x in zip(bufs, numels)])
+        if mode == "ranges":
+            Z.zero_z3_step(st.plan, reduce_b0=0, rows=rdev[0:3], row_strides=strides[0:3], live=st.live, g32=st.g32,
+                           pack_b0=3, grad_ptrs=gdev, packed=[st.block(st.packed, b) for b in range(3, 6)],
+                           check=check, gather_b0=6, gathered=[st.block(st.arena, b) for b in range(6, 8)],
+                           param_ptrs=ptrs, flag=st.flag)
+        else:
+            for b in range(0, 3):
+                Z.zero_reduce_shard(st.plan, b, rdev[b], strides[b], st.live, st.g32, st.flag)
+            for b in range(3, 6):
+                if check:
+                    Z.zero_pack_bucket_check(st.plan, b, gdev, st.block(st.packed, b), st.flag)
+                else:
+                    Z.zero_pack_bucket(st.plan, b, gdev, st.block(st.packed, b))
+            for b in range(6, 8):
+                Z.zero_unpack(st.plan, b, st.block(st.arena, b), ptrs)
+        torch.cuda.synchronize()
+        outs[mode] = (st.g32.clone(), st.packed.clone(), [t.clone() for t in bufs], int(st.flag.item()))
+        del st
+    a, b = outs["ranges"], outs["single"]
+    assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
+    assert torch.equal(a[1], b[1])
+    assert all(torch.equal(x, y) for x, y in zip(a[2], b[2]))
+    assert a[3] == b[3]
+    # against the oracle: g32 of buckets 0..2, the packed blocks of 3..5, the parameters of 6..7
+    g32 = np.full(pl.shard_len, -7.0, np.float32)
+    for bk in range(0, 3):
+        oracle.reduce_bucket(pl, bk, rows[bk][:, :int(pl.buckets[bk, oracle.B_STRIDE])].copy(), dtype, live, g32)
+    assert_same_f32(to_np32(a[0]), g32, "g32")
+    packed = to_np16(a[1])
+    for bk in range(3, 6):
+        # the oracle's pack over a block holding the same fill (dead parameters' slots keep it)
+        want = np.full((nd, int(pl.buckets[bk, oracle.B_STRIDE])), 0x0F0F, np.uint16)
+        oracle.pack_bucket(pl, bk, [g if l else None for g, l in zip(grads, live)], want)
+        assert np.array_equal(oracle_block(pl, packed, bk), want), bk
+    for i, x in enumerate(numels):
+        got = to_np16(a[2][i])
+        bk = int(pl.params[i, oracle.P_BUCKET])
+        if bk >= 6:
+            want = [None] * len(numels)
+            want[i] = np.zeros(x, np.uint16)
+            oracle.unpack_bucket(pl, bk, oracle_block(pl, arena, bk).copy(), want)
+            assert np.array_equal(got[1:1 + x], want[i]), i
+        else:
+            assert np.all(got == 0x1111), i
+        assert got[0] == 0x1111 and got[-1] == 0x1111, i
+
+
+def test_z3_step_arguments():
+    """Nothing to do is allowed; counts above the maximum or ranges outside the plan are refused
+    before anything runs, as are the per-bucket entry points' own errors."""
+    n = Z.Z3_MAX_BUCKETS + 2
+    numels = [100 + 8 * i for i in range(n)]
+    st = Z.ShardStep(numels, 8, 3, 0, BF16, groups=list(range(n)))
+    outs = [torch.full((x,), 0x2222, dtype=torch.int16, device=DEV) for x in numels]
+    ptrs = Z.ptr_table(outs)
+    Z.zero_z3_step(st.plan)
+    with pytest.raises(ValueError):  # more buckets than a piece holds (caught by the binding)
+        Z.zero_z3_step(st.plan, gather_b0=0, gathered=[st.block(st.arena, b) for b in range(n - 1)], param_ptrs=ptrs)
+    for b0 in (-1, n - 1):  # ranges reaching outside the plan
+        with pytest.raises(Z.ZeroError) as e:
+            Z.zero_z3_step(st.plan, gather_b0=b0, gathered=[st.arena, st.arena], param_ptrs=ptrs)
+        assert e.value.status == Z.ZERO_EINVAL, b0
+    big = torch.zeros(st.arena.numel() + 8, dtype=torch.int16, device=DEV)
+    with pytest.raises(Z.ZeroError) as e:  # a misaligned block (zero_unpack's own check)
+        Z.zero_z3_step(st.plan, gather_b0=0, gathered=[st.block(st.arena, 0), big[1:]], param_ptrs=ptrs)
+    assert e.value.status == Z.ZERO_EINVAL
+    with pytest.raises(Z.ZeroError) as e:  # the checked pack needs the flag
+        Z.zero_z3_step(st.plan, pack_b0=0, grad_ptrs=ptrs, packed=[st.block(st.packed, 0)], check=True)
+    assert e.value.status == Z.ZERO_EINVAL
+    torch.cuda.synchronize()
+    assert all(torch.all(t == 0x2222) for t in outs)
+    assert torch.all(st.packed == 0)

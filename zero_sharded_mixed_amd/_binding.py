@@ -27,8 +27,9 @@ EXPORTS = ("zero_plan_create", "zero_plan_create_grouped", "zero_plan_destroy", 
            "zero_pack_bucket", "zero_reduce_shard", "zero_overflow_check", "zero_adam_step", "zero_unpack",
            "zero_shard_init", "zero_pack_bucket_check", "zero_adam_prepare", "zero_reduce_adam_bucket",
            "zero_loss_scaler_init", "zero_loss_scaler_update", "zero_last_error", "zero_adam_step_noalloc",
-           "zero_z3_layer_step")
+           "zero_z3_layer_step", "zero_z3_step")
 ADAM_NOALLOC_MAX_PARAMS = 131072  # ZERO_ADAM_NOALLOC_MAX_PARAMS
+Z3_MAX_BUCKETS = 4                # ZERO_Z3_MAX_BUCKETS
 
 
 class ZeroError(RuntimeError):
@@ -57,6 +58,17 @@ class zero_loss_scaler(ctypes.Structure):
     _fields_ = [("scale", ctypes.c_float), ("good_steps", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
                 ("growth_factor", ctypes.c_float), ("backoff_factor", ctypes.c_float), ("min_scale", ctypes.c_float),
                 ("max_scale", ctypes.c_float), ("overflows", ctypes.c_int32)]
+
+
+class zero_z3_pieces(ctypes.Structure):
+    _fields_ = [("reduce_b0", ctypes.c_int64), ("reduce_n", ctypes.c_int64),
+                ("rows", ctypes.c_void_p * Z3_MAX_BUCKETS), ("row_stride", ctypes.c_int64 * Z3_MAX_BUCKETS),
+                ("live", ctypes.c_void_p), ("g32", ctypes.c_void_p),
+                ("pack_b0", ctypes.c_int64), ("pack_n", ctypes.c_int64), ("grad_ptrs", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p * Z3_MAX_BUCKETS), ("check", ctypes.c_int32),
+                ("gather_b0", ctypes.c_int64), ("gather_n", ctypes.c_int64),
+                ("gathered", ctypes.c_void_p * Z3_MAX_BUCKETS), ("param_ptrs", ctypes.c_void_p),
+                ("flag", ctypes.c_void_p)]
 
 
 class zero_adam_hparams(ctypes.Structure):
@@ -102,6 +114,7 @@ def lib() -> ctypes.CDLL:
         "zero_adam_step_noalloc": (i32, [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp, vp]),
         "zero_unpack": (i32, [vp, i64, vp, vp, vp]),
         "zero_z3_layer_step": (i32, [vp, i64, vp, i64, vp, vp, i64, vp, vp, i32, i64, vp, vp, vp, vp]),
+        "zero_z3_step": (i32, [vp, ctypes.POINTER(zero_z3_pieces), vp]),
         "zero_shard_init": (i32, [vp, vp, i32, vp, vp]),
         "zero_pack_bucket_check": (i32, [vp, i64, vp, vp, vp, vp]),
         "zero_adam_prepare": (i32, [vp, vp, vp, ctypes.POINTER(zero_adam_hparams), vp, vp]),
@@ -212,8 +225,8 @@ def _table(plan: "Plan", table: torch.Tensor, what: str, elem_size: int) -> int:
 
 class Plan:
     """Owns a zero_plan*; destroyed with the object (or by close()).  Keeps the sizes the
-    entry points' argument checks need: per-parameter numel, per-bucket row length and row
-    stride, the shard and arena lengths."""
+    entry points' argument checks need: per-parameter numel, per-bucket row stride and block
+    offset, the shard and arena lengths."""
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
@@ -228,10 +241,11 @@ class Plan:
             numels[i] = info.numel
         self.numels = numels
         bk = zero_bucket_info()
-        self.row_stride = []
+        self.row_stride, self.block_offset = [], []
         for b in range(self.n_buckets):
             _check(lib().zero_plan_bucket_info(self._h, b, ctypes.byref(bk)))
             self.row_stride.append(int(bk.row_stride))
+            self.block_offset.append(int(bk.block_offset))
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -370,6 +384,45 @@ def zero_unpack(plan: Plan, b: int, gathered: torch.Tensor, param_ptrs: torch.Te
     _check(lib().zero_unpack(plan.handle, b, _buf(plan, gathered, "zero_unpack: gathered", plan.block_elems(b),
                                                   elem_size=2),
                              _table(plan, param_ptrs, "zero_unpack: parameters", 2), _stream(stream)))
+
+
+def zero_z3_step(plan: Plan, reduce_b0: int = 0, rows: Sequence = (), row_strides: Sequence = (),
+                 live: Optional[torch.Tensor] = None, g32: Optional[torch.Tensor] = None, pack_b0: int = 0,
+                 grad_ptrs: Optional[torch.Tensor] = None, packed: Sequence = (), check: bool = False,
+                 gather_b0: int = 0, gathered: Sequence = (), param_ptrs: Optional[torch.Tensor] = None,
+                 flag: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One launch: the reduce of buckets reduce_b0 + j from rows[j] (row stride row_strides[j]),
+    the pack of buckets pack_b0 + j into packed[j], the unpack of buckets gather_b0 + j from
+    gathered[j] (empty sequences leave a kind out)."""
+    w = "zero_z3_step"
+    nr, nk, nu = len(rows), len(packed), len(gathered)
+    if len(row_strides) != nr:
+        raise ValueError(f"{w}: {nr} row buffers but {len(row_strides)} row strides")
+    if max(nr, nk, nu) > Z3_MAX_BUCKETS:
+        raise ValueError(f"{w}: at most {Z3_MAX_BUCKETS} buckets per piece")
+    z = zero_z3_pieces()
+    z.reduce_b0, z.reduce_n = reduce_b0, nr
+    for j in range(nr):
+        b = reduce_b0 + j
+        z.rows[j] = _buf(plan, rows[j], f"{w}: rows of bucket {b}", plan.rows_elems(b, row_strides[j]), elem_size=2)
+        z.row_stride[j] = int(row_strides[j])
+    if nr:
+        z.live = _buf(plan, live, w + ": live", plan.n, U8)
+        z.g32 = _buf(plan, g32, w + ": g32", plan.shard_numel, F32)
+    z.pack_b0, z.pack_n, z.check = pack_b0, nk, int(bool(check))
+    for j in range(nk):
+        z.packed[j] = _buf(plan, packed[j], f"{w}: packed block of bucket {pack_b0 + j}", plan.block_elems(pack_b0 + j),
+                           elem_size=2)
+    if nk:
+        z.grad_ptrs = _table(plan, grad_ptrs, w + ": gradients", 2)
+    z.gather_b0, z.gather_n = gather_b0, nu
+    for j in range(nu):
+        z.gathered[j] = _buf(plan, gathered[j], f"{w}: gathered block of bucket {gather_b0 + j}",
+                             plan.block_elems(gather_b0 + j), elem_size=2)
+    if nu:
+        z.param_ptrs = _table(plan, param_ptrs, w + ": parameters", 2)
+    z.flag = _buf(plan, flag, w + ": flag", 1, I32)
+    _check(lib().zero_z3_step(plan.handle, ctypes.byref(z), _stream(stream)))
 
 
 def zero_z3_layer_step(plan: Plan, reduce_b: int = -1, rows: Optional[torch.Tensor] = None, row_stride: int = 0,

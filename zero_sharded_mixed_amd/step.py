@@ -136,7 +136,8 @@ class Zero3Schedule:
     The gather of layer l is zero_unpack of bucket l from the all-gather block (the Nd ranks'
     rows of that layer).  Without prefetch its destination is one scratch buffer sized for the
     largest layer, so at most one layer's full parameters exist at a time, and everything runs
-    in order on the caller's stream.
+    in order on the caller's stream.  With batch=k the layers go k at a time, in k scratch slots
+    (k layers' full parameters at a time).
 
     With prefetch=True the gathers run on a second stream into two scratch buffers (layer l in
     buffer l % 2), so the gather of the next layer overlaps the use of the current one and, in
@@ -147,15 +148,23 @@ class Zero3Schedule:
     so a pass can also be captured into a graph.  At most two layers' parameters exist at a
     time.  `use` callbacks run with the caller's stream current."""
 
-    def __init__(self, st: ShardStep, prefetch: bool = False, fused: bool = False):
-        """fused=True (one stream only): each backward step is one zero_z3_layer_step launch --
-        the reduce of layer l + 1, the pack of layer l and the gather of layer l - 1 share a
-        launch -- instead of three launches per layer."""
+    def __init__(self, st: ShardStep, prefetch: bool = False, fused: bool = False, batch: int = 1):
+        """fused=True (one stream only): each backward step is one zero_z3_step launch -- the
+        reduce of layer l + 1, the pack of layer l and the gather of layer l - 1 share a launch --
+        instead of three launches per layer.  batch=k (fused only): every launch handles k
+        consecutive layers -- the forward pass gathers layers [l, l + k) together, a backward
+        step packs [l, l + k), gathers [l - k, l) and reduces [l + k, l + 2k) -- so that k layers
+        share one launch tail; the scratch then holds k layers (layer l at slot l mod k)."""
         if prefetch and fused:
             raise ValueError("the fused backward runs on one stream (prefetch=False)")
+        if not 1 <= batch <= B.Z3_MAX_BUCKETS:
+            raise ValueError(f"batch must be in 1..{B.Z3_MAX_BUCKETS}")
+        if batch > 1 and not fused:
+            raise ValueError("batches of layers need the fused schedule (fused=True)")
         self.st = st
         self.prefetch = prefetch
         self.fused = fused
+        self.batch = batch
         nb = len(st.buckets)
         infos = [B.zero_plan_param_info(st.plan, i) for i in range(st.n)]
         self.layers = [list(range(int(bk.first_param), int(bk.first_param + bk.n_params))) for bk in st.buckets]
@@ -164,7 +173,7 @@ class Zero3Schedule:
         # each parameter 16-byte aligned inside the scratch (the unpack's wide path)
         per = [sum((x + 7) // 8 * 8 for x in xs) for xs in self.numel]
         need = max(per + [biggest, 8])
-        nbuf = 2 if prefetch else 1
+        nbuf = 2 if prefetch else batch
         self.buffer_numel = need
         self.scratch = torch.zeros(nbuf * need, dtype=torch.int16, device=st.device)
         self.views, self.tables = [], []
@@ -178,6 +187,18 @@ class Zero3Schedule:
                 full[i] = v
             self.views.append(views)
             self.tables.append(B.ptr_table(full, device=st.device))
+        # batches of layers [lo, hi): one destination table per batch
+        self.batches = [(lo, min(lo + batch, nb)) for lo in range(0, nb, batch)]
+        self.batch_tables = []
+        for lo, hi in self.batches:
+            if hi - lo == 1:
+                self.batch_tables.append(self.tables[lo])
+                continue
+            full = [None] * st.n
+            for lid in range(lo, hi):
+                for i, v in zip(self.layers[lid], self.views[lid]):
+                    full[i] = v
+            self.batch_tables.append(B.ptr_table(full, device=st.device))
         self.order: list = []  # layers in the order they were gathered
         if prefetch:
             self.side = torch.cuda.Stream(device=st.device)
@@ -229,6 +250,16 @@ class Zero3Schedule:
     # -- passes --------------------------------------------------------------------------------
 
     def forward(self, use: Optional[Callable[[int, list], None]] = None, stream=None) -> None:
+        if self.batch > 1:
+            st = self.st
+            for j, (lo, hi) in enumerate(self.batches):
+                B.zero_z3_step(st.plan, gather_b0=lo, gathered=[st.block(st.arena, l) for l in range(lo, hi)],
+                               param_ptrs=self.batch_tables[j], stream=stream)
+                self.order.extend(range(lo, hi))
+                if use is not None:
+                    for lid in range(lo, hi):
+                        use(lid, self.views[lid])
+            return
         if not self.prefetch:
             for lid in range(len(self.layers)):
                 params = self.gather(lid, stream=stream)
@@ -279,23 +310,33 @@ class Zero3Schedule:
             self._join(main)
 
     def _backward_fused(self, grads_of, rows_of, use, check, out, stream) -> None:
-        """Layers L-1 .. 0; before step l's launch, layer l's parameters are in the scratch (the
-        last layer's since the forward pass) and `use` runs on them; the launch then packs layer
-        l's gradients, gathers layer l - 1 into the scratch and reduces layer l + 1 (packed one
-        step earlier).  A last launch reduces layer 0."""
+        """Batches of layers J-1 .. 0 (one layer each unless batch > 1); before step j's launch,
+        batch j's parameters are in the scratch (the last batch's since the forward pass) and
+        `use` runs on its layers, last first; the launch then packs batch j's gradients
+        (grads_of(lo) must name those of the whole batch [lo, hi)), gathers batch j - 1 into
+        the scratch and reduces batch j + 1 (packed one step earlier).  A last launch reduces
+        batch 0."""
         st = self.st
-        last = len(self.layers) - 1
-        for lid in range(last, -2, -1):
-            if lid >= 0 and use is not None:
-                use(lid, self.views[lid])
-            rb = lid + 1 if lid + 1 <= last else -1
-            pb = lid
-            gb = lid - 1 if lid >= 1 else -1
-            rows, stride = rows_of(rb) if rb >= 0 else (None, 0)
-            B.zero_z3_layer_step(st.plan, reduce_b=rb, rows=rows, row_stride=stride, live=st.live, g32=st.g32,
-                                 pack_b=pb, grad_ptrs=grads_of(pb) if pb >= 0 else None,
-                                 packed=st.block(out, pb) if pb >= 0 else None, check=check, gather_b=gb,
-                                 gathered=st.block(st.arena, gb) if gb >= 0 else None,
-                                 param_ptrs=self.tables[gb] if gb >= 0 else None, flag=st.flag, stream=stream)
-            if gb >= 0:
-                self.order.append(gb)
+        J = len(self.batches)
+        for j in range(J - 1, -2, -1):
+            if j >= 0 and use is not None:
+                lo, hi = self.batches[j]
+                for lid in range(hi - 1, lo - 1, -1):
+                    use(lid, self.views[lid])
+            kw = {}
+            if j + 1 < J:
+                lo, hi = self.batches[j + 1]
+                rs = [rows_of(b) for b in range(lo, hi)]
+                kw.update(reduce_b0=lo, rows=[r for r, _ in rs], row_strides=[x for _, x in rs], live=st.live,
+                          g32=st.g32)
+            if j >= 0:
+                lo, hi = self.batches[j]
+                kw.update(pack_b0=lo, grad_ptrs=grads_of(lo), packed=[st.block(out, b) for b in range(lo, hi)],
+                          check=check)
+            if j >= 1:
+                lo, hi = self.batches[j - 1]
+                kw.update(gather_b0=lo, gathered=[st.block(st.arena, b) for b in range(lo, hi)],
+                          param_ptrs=self.batch_tables[j - 1])
+            B.zero_z3_step(st.plan, flag=st.flag, stream=stream, **kw)
+            if j >= 1:
+                self.order.extend(range(hi - 1, lo - 1, -1))
