@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kBlock) void reduce_adam_kernel(DevPlan P, int64_t 
             v0 = load4f(v + x), v1 = load4f(v + x + 4);
         }
         float acc[8];
-        reduce_rows8<DT>(rows + c, P.nd, row_stride, acc);
+        reduce_rows8<DT, true>(rows + (x0 - b_base), threadIdx.x * kChunk, P.nd, row_stride, acc);
         if (vec) {
             // eight columns of one live parameter: the vector update
             const float2 sc = whole ? sc_u : scal[i];

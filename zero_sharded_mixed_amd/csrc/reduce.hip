@@ -6,8 +6,9 @@
 // Each thread owns 8 consecutive columns of the bucket row and keeps 8 fp32 accumulators.
 // It reads the 16 bytes of every rank's row at those columns (aligned dwordx4: rows start on
 // 16-byte boundaries), converts exactly to fp32 and adds in ascending rank order, seeded with
-// rank 0's value — the fixed order that makes the sums bit-reproducible.  Loads of the next
-// ranks are issued ahead of the adds (kAhead rows in flight) so HBM latency overlaps.
+// rank 0's value — the fixed order that makes the sums bit-reproducible.  The rows are read
+// in groups of eight, and the next group's loads are issued before the current group's adds,
+// so HBM latency overlaps the arithmetic.
 // Columns of parameters without a gradient are skipped before any row is read.  The overflow
 // flag is ORed once per wavefront (a ballot, then one atomic), only when a value is found.
 #include "zs_reduce.h"
@@ -19,7 +20,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_bas
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
-    reduce_body<DT>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
+    reduce_body<DT, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,
