@@ -709,10 +709,11 @@ def cpu_baseline(w, max_elems: int, device="cuda"):
 
 KERNEL_KEYS = (("probe_adam_streams_kernel", "probe_adam_streams"), ("probe_copy_kernel", "probe_copy"),
                ("probe_read_kernel", "probe_read"), ("probe_write_kernel", "probe_write"),
-               ("z3_layer_kernel", "z3_layer"), ("adam_prepare_kernel", "adam_prepare"), ("reduce_adam_kernel", "reduce_adam"),
+               ("z3_kernel", "z3"), ("adam_prepare_kernel", "adam_prepare"), ("reduce_adam_kernel", "reduce_adam"),
                ("unpack_kernel", "unpack"), ("pack_kernel", "pack"), ("reduce_kernel", "reduce"),
                ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"))
-SHORT_NAMES = tuple(s for _, s in KERNEL_KEYS) + ("pack_check",)
+SHORT_NAMES = tuple(s for _, s in KERNEL_KEYS) + ("pack_check",) + tuple(
+    f"z3 (up to {k} bucket{'s' if k != 1 else ''} per kind)" for k in (1, 2, 4))
 
 
 def _short(name: str) -> str:
@@ -720,6 +721,10 @@ def _short(name: str) -> str:
         if key in name:
             if short == "pack" and ("true>" in name or "Lb1E" in name):
                 return "pack_check"  # the pack with the input check (fused path)
+            if short == "z3":  # the ZeRO-3 launch, by buckets per kind (template argument K)
+                k = (name.split("Z3Parts<")[1].split(">")[0] if "Z3Parts<" in name else
+                     name.split("Z3PartsILi")[1].split("E")[0] if "Z3PartsILi" in name else "?")
+                return f"z3 (up to {k} bucket{'s' if k != '1' else ''} per kind)"
             return short
     return name[:60]
 
