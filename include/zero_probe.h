@@ -8,7 +8,8 @@
  * denominator of every roofline fraction stays the HBM peak).
  *
  * Every probe launches a one-shot grid (one block of 256 threads per 4 KiB of the first
- * stream, one 16-byte chunk per thread per stream, like the pipeline kernels) on `stream`,
+ * stream, one 16-byte chunk per thread per stream, ordinary loads and nontemporal stores,
+ * like the pipeline kernels) on `stream`,
  * never allocates and never synchronises.  Sizes are in bytes (multiples of 16) or elements
  * (multiples of 8).  Buffers are caller-owned device memory, 16-byte aligned, and must stay
  * allocated until the launched work has finished.  Every call returns ZERO_OK, ZERO_EINVAL

@@ -112,9 +112,15 @@ __device__ __forceinline__ uint4 load16_off(const uint16_t* base, uint32_t byte_
     const zs_u32x4 w = *(const ZS_GLOBAL zs_u32x4*)((const ZS_GLOBAL char*)base + byte_off);
     return make_uint4(w.x, w.y, w.z, w.w);
 }
+// The 16-byte stores are nontemporal (the nt bit): every kernel writes each output once and no
+// later work of the same kernel reads it.  Measured on MI355X against ordinary stores, in one
+// process: unpack 5-8% faster, pack 0.4-3%, Adam 3%, the fused reduce + Adam 2-4%, the reduce
+// 1%.  (Nontemporal loads are the opposite: a load instruction that covers only parts of the
+// cache lines it touches -- the unpack's second granule, Adam's two half-lines per thread --
+// then fetches those lines again, and the kernels ran 1-17% slower.)
 __device__ __forceinline__ void store16(void* p, const uint4& v) {
     zs_u32x4 w = {v.x, v.y, v.z, v.w};
-    *gptr(reinterpret_cast<zs_u32x4*>(p)) = w;
+    __builtin_nontemporal_store(w, gptr(reinterpret_cast<zs_u32x4*>(p)));
 }
 __device__ __forceinline__ float4 load4f(const float* p) {
     const zs_f32x4 w = *gptr(reinterpret_cast<const zs_f32x4*>(p));
@@ -122,7 +128,7 @@ __device__ __forceinline__ float4 load4f(const float* p) {
 }
 __device__ __forceinline__ void store4f(float* p, const float4& v) {
     zs_f32x4 w = {v.x, v.y, v.z, v.w};
-    *gptr(reinterpret_cast<zs_f32x4*>(p)) = w;
+    __builtin_nontemporal_store(w, gptr(reinterpret_cast<zs_f32x4*>(p)));
 }
 
 // Sixteen bytes from any 2-byte aligned address: one global_load_dwordx4, the memory system
@@ -136,7 +142,7 @@ __device__ __forceinline__ uint4 load16_any(const uint16_t* p) {
 
 __device__ __forceinline__ void store16_any(uint16_t* p, const uint4& v) {
     zs_u32x4_a2 w = {v.x, v.y, v.z, v.w};
-    *(ZS_GLOBAL zs_u32x4_a2*)p = w;
+    __builtin_nontemporal_store(w, (ZS_GLOBAL zs_u32x4_a2*)p);
 }
 
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

@@ -1,7 +1,7 @@
 // bandwidth.hip — memory-bandwidth probes in the pipeline kernels' access patterns (see
 // include/zero_probe.h).  Trivial arithmetic, the same launch shape as the pipeline: a one-shot
 // grid of 256-thread blocks, each thread one 16-byte chunk per stream, global (not flat)
-// 16-byte loads and stores.
+// 16-byte loads and nontemporal 16-byte stores, as in the pipeline kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,9 +16,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld(const void* p) { return *(const ZP_GLOBAL u32x4*)p; }
-__device__ __forceinline__ void st(void* p, u32x4 v) { *(ZP_GLOBAL u32x4*)p = v; }
+__device__ __forceinline__ void st(void* p, u32x4 v) { __builtin_nontemporal_store(v, (ZP_GLOBAL u32x4*)p); }
 __device__ __forceinline__ f32x4 ldf(const float* p) { return *(const ZP_GLOBAL f32x4*)p; }
-__device__ __forceinline__ void stf(float* p, f32x4 v) { *(ZP_GLOBAL f32x4*)p = v; }
+__device__ __forceinline__ void stf(float* p, f32x4 v) { __builtin_nontemporal_store(v, (ZP_GLOBAL f32x4*)p); }
 
 // chunks: 16-byte chunks of the stream; one per thread per iteration of the grid-stride loop
 __global__ __launch_bounds__(kBlock) void probe_read_kernel(const u32x4* __restrict__ src, int64_t chunks,
