@@ -114,14 +114,17 @@ constexpr int kStageMax = ZS_STAGE_MAX;
 //  * mixed tiles (several parameters, padding, the row gap): kMixRows rows of one tile per
 //    block, tiles varying fastest, by runs (above); they come first, so that these heavier
 //    blocks do not form the launch's tail;
-//  * whole tiles (a tile inside one parameter): kWholeRows rows of one tile per block, rows
-//    varying fastest.  Each block moves only kWholeRows * 4 KB behind a chain of dependent loads
+//  * whole tiles (a tile inside one parameter): kWholeRows rows of one tile per block, tiles
+//    varying fastest, so that consecutive blocks read and write consecutive 4 KB pieces of the
+//    same rows.  Each block moves only kWholeRows * 4 KB behind a chain of dependent loads
 //    (list entry -> parameter fields and gradient pointer -> data), so the chain is kept at that
 //    length (the list entry carries the parameter) and the rows of a block share it.
-// Measured on MI355X: one row per block, four, or tiles varying fastest, lose 2-20% on the
-// whole-tile lists; a fixed grid that prefetches the next item loses 10-40% against this
-// one-block-per-item grid; 4 rows per mixed block are 1% slower than 8 on the ragged list,
-// 16 rows 4-38% slower (the run's 16 loads in flight cost registers, hence occupancy).
+// Measured on MI355X, with the nontemporal stores: tiles varying fastest are 8% faster than
+// rows varying fastest on the 7.5B list (Nd = 64) and level elsewhere (with ordinary stores
+// rows-fastest had been 2-20% ahead); one or four rows per block lose 3-14%; a fixed grid that
+// prefetches the next item loses 10-40% against this one-block-per-item grid; 4 rows per mixed
+// block are 1% slower than 8 on the ragged list, 16 rows up to 50% slower (the run's 16 loads in
+// flight cost registers, hence occupancy).
 // tiles: the bucket's n_whole whole tiles, then its n_mixed mixed tiles (plan tables).
 #ifndef ZS_MIX_ROWS
 #define ZS_MIX_ROWS 8
@@ -143,9 +146,9 @@ struct WholeItem {
 __device__ __forceinline__ WholeItem whole_item(const DevPlan& P, const int64_t* __restrict__ tiles,
                                                 const uint16_t* const* __restrict__ grads, int64_t w, int64_t n_wrg,
                                                 int64_t n_whole) {
-    // rows vary fastest: consecutive blocks take the row groups of one tile
-    const int64_t jw = n_whole * n_wrg <= int64_t(UINT32_MAX) ? int64_t(uint32_t(w) / uint32_t(n_wrg)) : w / n_wrg;
-    const int64_t rg = w - jw * n_wrg;
+    // tiles vary fastest: consecutive blocks take consecutive whole tiles of one row group
+    const int64_t rg = n_whole * n_wrg <= int64_t(UINT32_MAX) ? int64_t(uint32_t(w) / uint32_t(n_whole)) : w / n_whole;
+    const int64_t jw = w - rg * n_whole;
     const int64_t j = ld_const(tiles, 2 * jw), i = ld_const(tiles, 2 * jw + 1);  // the tile, its parameter
     return WholeItem{rg * kWholeRows, j << kTileShift, ld_const(P.off, i), ld_const(P.s, i), ld_const(P.numel, i),
                      ld_const(grads, i)};
