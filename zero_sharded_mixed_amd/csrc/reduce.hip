@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_bas
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
-    reduce_body<DT, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
+    reduce_body<DT, true, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,

@@ -108,8 +108,13 @@ __device__ __forceinline__ uint4 load16(const void* p) {
 // The same at base + byte_off with base uniform across the wavefront: the address is one
 // scalar base and a 32-bit per-lane offset, so a thread holding loads of many rows in flight
 // spends one register on their addresses rather than two per row.
+// NT: a nontemporal load, for streams whose every load instruction covers whole cache lines.
+template <bool NT = false>
 __device__ __forceinline__ uint4 load16_off(const uint16_t* base, uint32_t byte_off) {
-    const zs_u32x4 w = *(const ZS_GLOBAL zs_u32x4*)((const ZS_GLOBAL char*)base + byte_off);
+    const ZS_GLOBAL zs_u32x4* p = (const ZS_GLOBAL zs_u32x4*)((const ZS_GLOBAL char*)base + byte_off);
+    zs_u32x4 w;
+    if constexpr (NT) w = __builtin_nontemporal_load(p);
+    else w = *p;
     return make_uint4(w.x, w.y, w.z, w.w);
 }
 // The 16-byte stores are nontemporal (the nt bit): every kernel writes each output once and no
@@ -214,7 +219,10 @@ __device__ __forceinline__ bool non_finite(float f) { return (__float_as_uint(f)
 // in flight) and the last partial group is loaded whole: measured on MI355X 1-4% faster in a
 // reduce of its own, but the two groups in registers take 160 VGPRs, which a kernel that shares
 // its registers with the pack and the unpack cannot afford (the ZeRO-3 layer launch lost 5%).
-// Without PIPE: row 0, then groups from row 1, then the rest one row at a time.
+// Without PIPE: row 0, then groups from row 1, then the rest one row at a time.  NT makes the
+// row loads nontemporal (each wave's load covers 1 KB of whole lines): 0.5-3.4% faster in the
+// reduce of its own on all four lists; in the fused reduce + Adam, which also streams p32, m
+// and v, 3% slower at Nd = 64, so it is the reduce's alone.
 constexpr int kAhead = 8;
 template <int DT>
 __device__ __forceinline__ void reduce_group_adds(float (&acc)[8], const uint4 (&v)[kAhead], bool first) {
@@ -223,12 +231,13 @@ __device__ __forceinline__ void reduce_group_adds(float (&acc)[8], const uint4 (
 #pragma unroll
     for (int u = 1; u < kAhead; ++u) accumulate8<DT, false>(acc, v[u]);
 }
+template <bool NT>
 __device__ __forceinline__ void reduce_group_loads(uint4 (&v)[kAhead], const uint16_t* rows_u, uint32_t lane_bytes,
                                                    int64_t k, int64_t row_stride) {
 #pragma unroll
-    for (int u = 0; u < kAhead; ++u) v[u] = load16_off(rows_u + (k + u) * row_stride, lane_bytes);
+    for (int u = 0; u < kAhead; ++u) v[u] = load16_off<NT>(rows_u + (k + u) * row_stride, lane_bytes);
 }
-template <int DT, bool PIPE>
+template <int DT, bool PIPE, bool NT = false>
 __device__ __forceinline__ void reduce_rows8(const uint16_t* rows_u, uint32_t lane, int64_t nd, int64_t row_stride,
                                              float (&acc)[8]) {
     const uint32_t lb = lane * 2u;
@@ -237,25 +246,25 @@ __device__ __forceinline__ void reduce_rows8(const uint16_t* rows_u, uint32_t la
     if constexpr (PIPE) {
         uint4 b[kAhead];
         if (ng > 0) {
-            reduce_group_loads(a, rows_u, lb, 0, row_stride);
+            reduce_group_loads<NT>(a, rows_u, lb, 0, row_stride);
             for (int64_t g = 0;; g += 2) {  // a holds group g, b group g + 1
-                if (g + 1 < ng) reduce_group_loads(b, rows_u, lb, (g + 1) * kAhead, row_stride);
+                if (g + 1 < ng) reduce_group_loads<NT>(b, rows_u, lb, (g + 1) * kAhead, row_stride);
                 reduce_group_adds<DT>(acc, a, g == 0);
                 if (g + 1 >= ng) break;
-                if (g + 2 < ng) reduce_group_loads(a, rows_u, lb, (g + 2) * kAhead, row_stride);
+                if (g + 2 < ng) reduce_group_loads<NT>(a, rows_u, lb, (g + 2) * kAhead, row_stride);
                 reduce_group_adds<DT>(acc, b, false);
                 if (g + 2 >= ng) break;
             }
         }
     } else {
         // fewest registers: row 0, then groups of kAhead rows from row 1, then one row at a time
-        accumulate8<DT, true>(acc, load16_off(rows_u, lb));
+        accumulate8<DT, true>(acc, load16_off<NT>(rows_u, lb));
         int64_t k = 1;
         for (; k + kAhead <= nd; k += kAhead) {
-            reduce_group_loads(a, rows_u, lb, k, row_stride);
+            reduce_group_loads<NT>(a, rows_u, lb, k, row_stride);
             reduce_group_adds<DT>(acc, a, false);
         }
-        for (; k < nd; ++k) accumulate8<DT, false>(acc, load16_off(rows_u + k * row_stride, lb));
+        for (; k < nd; ++k) accumulate8<DT, false>(acc, load16_off<NT>(rows_u + k * row_stride, lb));
         return;
     }
     const int rem = int(nd - ng * kAhead);
@@ -263,7 +272,7 @@ __device__ __forceinline__ void reduce_rows8(const uint16_t* rows_u, uint32_t la
     const int64_t k0 = ng * kAhead;
 #pragma unroll
     for (int u = 0; u < kAhead; ++u)
-        if (u < rem) a[u] = load16_off(rows_u + (k0 + u) * row_stride, lb);
+        if (u < rem) a[u] = load16_off<NT>(rows_u + (k0 + u) * row_stride, lb);
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
         if (u >= rem) break;
