@@ -492,7 +492,7 @@ def ceilings(device, adam_cols: int, pack_bytes: int, reps: int = 10):
            "write": timed(lambda: probe.write(dst), nb),
            "copy": timed(lambda: probe.copy(src, dst), 2 * nb)}
     del src, dst
-    n = adam_cols // 8 * 8
+    n = max(adam_cols // 2048, 1) * 2048  # the probe takes whole 2048-column spans
     f32 = dict(dtype=torch.float32, device=device)
     g, p, m, v = (torch.zeros(n, **f32) for _ in range(4))
     lp = torch.zeros(n, dtype=torch.int16, device=device)

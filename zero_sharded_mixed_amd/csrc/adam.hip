@@ -106,6 +106,50 @@ __device__ __forceinline__ void adam_cols(const AdamK& K, const AdamArgs& A, int
     }
 }
 
+// A whole span of kBlock * COLS columns of one live parameter, lane-strided: in pass q the
+// block's threads take consecutive 4-column groups of the span's q-th kBlock * 4 columns, so
+// that every load and store instruction of a wavefront covers 1 KB (512 B for the 16-bit
+// parameters) of whole cache lines, and the loads can be nontemporal.  Measured on MI355X
+// against 8 consecutive columns per thread (two half-line instructions per array): 5-8%
+// faster on the 7.5B, GPT-2 and Llama lists; the layout alone, with ordinary loads, is level.
+__device__ __forceinline__ float4 load4f_nt(const float* p) {
+    const zs_f32x4 w = __builtin_nontemporal_load(gptr(reinterpret_cast<const zs_f32x4*>(p)));
+    return make_float4(w.x, w.y, w.z, w.w);
+}
+template <int DT, int COLS>
+__device__ __forceinline__ void adam_span(const AdamK& K, const AdamArgs& A, int64_t x0, float2 sc, uint16_t* lp0) {
+    constexpr int V = COLS / 4;
+    float4 g4[V], p4[V], m4[V], v4[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+        const int64_t x = x0 + int64_t(q) * kBlock * 4 + int64_t(threadIdx.x) * 4;
+        g4[q] = load4f_nt(A.g32 + x);
+        p4[q] = load4f_nt(A.p32 + x);
+        m4[q] = load4f_nt(A.m + x);
+        v4[q] = load4f_nt(A.v + x);
+    }
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+        const int64_t xo = int64_t(q) * kBlock * 4 + int64_t(threadIdx.x) * 4;
+        float* gq = &g4[q].x;
+        float* pq = &p4[q].x;
+        float* mq = &m4[q].x;
+        float* vq = &v4[q].x;
+        uint16_t h[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            adam_elem(K, gq[t], pq[t], mq[t], vq[t], sc.x, sc.y);
+            h[t] = from_f32<DT>(pq[t]);
+        }
+        store4f(A.p32 + x0 + xo, p4[q]);
+        store4f(A.m + x0 + xo, m4[q]);
+        store4f(A.v + x0 + xo, v4[q]);
+        __builtin_nontemporal_store(
+            uint64_t(uint32_t(h[0]) | (uint32_t(h[1]) << 16)) | (uint64_t(uint32_t(h[2]) | (uint32_t(h[3]) << 16)) << 32),
+            gptr(reinterpret_cast<uint64_t*>(lp0 + xo)));
+    }
+}
+
 // One block per span of kBlock * COLS shard columns.
 template <int DT, int COLS>
 __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int64_t n_spans) {
@@ -126,7 +170,7 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int
         if (iu < P.n && off <= x0 && end >= x0 + kSpan) {
             if (!lv) continue;
             const int64_t O = ld_const(P.b_base, bu);
-            adam_cols<DT, COLS>(K, A, x, sc, A.arena + P.nd * O + P.rank * ld_const(P.b_stride, bu) + (x - O));
+            adam_span<DT, COLS>(K, A, x0, sc, A.arena + P.nd * O + P.rank * ld_const(P.b_stride, bu) + (x0 - O));
             continue;
         }
         if (x >= P.shard_numel) continue;

@@ -71,4 +71,6 @@ def adam_streams(g, p, m, v, lp, stream=None) -> None:
     for t, es in ((g, 4), (p, 4), (m, 4), (v, 4), (lp, 2)):
         if t.numel() < n or t.element_size() != es:
             raise ValueError("adam_streams: four fp32 arrays and one 16-bit array of n elements expected")
+    if n % 2048:
+        raise ValueError("adam_streams: n must be a multiple of 2048 (whole 2048-column spans)")
     _ok(lib().zero_probe_adam_streams(_p(g), _p(p), _p(m), _p(v), _p(lp), n, _s(stream)), "zero_probe_adam_streams")

@@ -1,7 +1,9 @@
 // bandwidth.hip — memory-bandwidth probes in the pipeline kernels' access patterns (see
 // include/zero_probe.h).  Trivial arithmetic, the same launch shape as the pipeline: a one-shot
 // grid of 256-thread blocks, each thread one 16-byte chunk per stream, global (not flat)
-// 16-byte loads and nontemporal 16-byte stores, as in the pipeline kernels.
+// 16-byte accesses.  Every load and store instruction of a wavefront covers 1 KB of whole cache
+// lines, and all of them are nontemporal: the fastest form of each pattern on this part (the
+// pipeline kernels use the same form wherever their data is aligned that way).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,9 +17,9 @@ constexpr int64_t kMaxBlocks = int64_t(1) << 23;  // fewer than 2^32 work-items 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ u32x4 ld(const void* p) { return *(const ZP_GLOBAL u32x4*)p; }
+__device__ __forceinline__ u32x4 ld(const void* p) { return __builtin_nontemporal_load((const ZP_GLOBAL u32x4*)p); }
 __device__ __forceinline__ void st(void* p, u32x4 v) { __builtin_nontemporal_store(v, (ZP_GLOBAL u32x4*)p); }
-__device__ __forceinline__ f32x4 ldf(const float* p) { return *(const ZP_GLOBAL f32x4*)p; }
+__device__ __forceinline__ f32x4 ldf(const float* p) { return __builtin_nontemporal_load((const ZP_GLOBAL f32x4*)p); }
 __device__ __forceinline__ void stf(float* p, f32x4 v) { __builtin_nontemporal_store(v, (ZP_GLOBAL f32x4*)p); }
 
 // chunks: 16-byte chunks of the stream; one per thread per iteration of the grid-stride loop
@@ -43,25 +45,26 @@ __global__ __launch_bounds__(kBlock) void probe_copy_kernel(const u32x4* __restr
         st(dst + c, ld(src + c));
 }
 
-// groups: 8-column groups; thread = one group (two 16-byte accesses per fp32 stream)
+// groups: spans of 2048 columns; a block takes one span, and in each of two passes its threads
+// take consecutive 4-column groups of one half (Adam's lane-strided layout: every instruction of
+// a wavefront covers whole lines of each stream, 8 bytes per lane for the 16-bit stream)
 __global__ __launch_bounds__(kBlock) void probe_adam_streams_kernel(const float* __restrict__ g,
                                                                     float* __restrict__ p, float* __restrict__ m,
                                                                     float* __restrict__ v, uint16_t* __restrict__ lp,
-                                                                    int64_t groups) {
-    for (int64_t q = blockIdx.x * int64_t(kBlock) + threadIdx.x; q < groups; q += int64_t(gridDim.x) * kBlock) {
-        const int64_t x = 8 * q;
-        const f32x4 g0 = ldf(g + x), g1 = ldf(g + x + 4);
-        f32x4 p0 = ldf(p + x), p1 = ldf(p + x + 4);
-        f32x4 m0 = ldf(m + x), m1 = ldf(m + x + 4);
-        f32x4 v0 = ldf(v + x), v1 = ldf(v + x + 4);
-        p0 += g0, p1 += g1, m0 += g0, m1 += g1, v0 += g0, v1 += g1;
-        stf(p + x, p0), stf(p + x + 4, p1);
-        stf(m + x, m0), stf(m + x + 4, m1);
-        stf(v + x, v0), stf(v + x + 4, v1);
-        const u32x4 a = __builtin_bit_cast(u32x4, p0), b = __builtin_bit_cast(u32x4, p1);
-        const u32x4 h = {(a.x >> 16) | (a.y & 0xffff0000u), (a.z >> 16) | (a.w & 0xffff0000u),
-                         (b.x >> 16) | (b.y & 0xffff0000u), (b.z >> 16) | (b.w & 0xffff0000u)};
-        st(lp + x, h);
+                                                                    int64_t spans) {
+    for (int64_t sp = blockIdx.x; sp < spans; sp += gridDim.x) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t x = sp * (8 * kBlock) + h * (4 * kBlock) + 4 * int64_t(threadIdx.x);
+            const f32x4 g0 = ldf(g + x);
+            f32x4 p0 = ldf(p + x), m0 = ldf(m + x), v0 = ldf(v + x);
+            p0 += g0, m0 += g0, v0 += g0;
+            stf(p + x, p0), stf(m + x, m0), stf(v + x, v0);
+            const u32x4 a = __builtin_bit_cast(u32x4, p0);
+            const uint64_t w = uint64_t((a.x >> 16) | (a.y & 0xffff0000u)) |
+                               (uint64_t((a.z >> 16) | (a.w & 0xffff0000u)) << 32);
+            __builtin_nontemporal_store(w, (ZP_GLOBAL uint64_t*)(lp + x));
+        }
     }
 }
 
@@ -104,9 +107,10 @@ extern "C" zero_status zero_probe_copy(const void* d_src, void* d_dst, int64_t b
 
 extern "C" zero_status zero_probe_adam_streams(const float* d_g, float* d_p, float* d_m, float* d_v, uint16_t* d_lp,
                                                int64_t n, void* stream) {
-    if (!d_g || !d_p || !d_m || !d_v || !d_lp || n <= 0 || n % 8) return ZERO_EINVAL;
+    if (!d_g || !d_p || !d_m || !d_v || !d_lp || n <= 0 || n % (8 * kBlock)) return ZERO_EINVAL;
     if (!a16(d_g) || !a16(d_p) || !a16(d_m) || !a16(d_v) || !a16(d_lp)) return ZERO_EINVAL;
-    const int64_t groups = n / 8;
-    probe_adam_streams_kernel<<<grid(groups), kBlock, 0, (hipStream_t)stream>>>(d_g, d_p, d_m, d_v, d_lp, groups);
+    const int64_t spans = n / (8 * kBlock);
+    const int g = int(spans < kMaxBlocks ? spans : kMaxBlocks);
+    probe_adam_streams_kernel<<<g, kBlock, 0, (hipStream_t)stream>>>(d_g, d_p, d_m, d_v, d_lp, spans);
     return launched();
 }
