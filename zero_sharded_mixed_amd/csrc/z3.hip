@@ -30,29 +30,35 @@ struct Z3Parts {
     UnpackLaunch u[K];
 };
 
-template <int DT, bool CHECK, int K>
+// KINDS: the kinds of parts compiled in (1 reduce, 2 pack, 4 unpack): a launch of gathers
+// only (the forward pass) then carries neither the reduce's nor the pack's registers.
+template <int DT, bool CHECK, int K, int KINDS>
 __global__ __launch_bounds__(kBlock) void z3_kernel(DevPlan P, Z3Parts<K> Z) {
-    __shared__ PackShared sh;
     int64_t b = blockIdx.x;
+    if constexpr ((KINDS & 1) != 0) {
 #pragma unroll
-    for (int p = 0; p < K; ++p) {
-        const ReduceLaunch& R = Z.r[p];
-        if (b < R.blocks) {
-            reduce_body<DT, false, false>(P, R.b_base, R.b_row, R.tile0, R.n_tile, R.rows, R.row_stride, R.live, R.g32, R.flag, b,
-                            R.blocks);
-            return;
+        for (int p = 0; p < K; ++p) {
+            const ReduceLaunch& R = Z.r[p];
+            if (b < R.blocks) {
+                reduce_body<DT, false, false>(P, R.b_base, R.b_row, R.tile0, R.n_tile, R.rows, R.row_stride, R.live,
+                                              R.g32, R.flag, b, R.blocks);
+                return;
+            }
+            b -= R.blocks;
         }
-        b -= R.blocks;
     }
+    if constexpr ((KINDS & 2) != 0) {
+        __shared__ PackShared sh;
 #pragma unroll
-    for (int p = 0; p < K; ++p) {
-        const PackLaunch& L = Z.k[p];
-        if (b < L.blocks) {
-            pack_body<CHECK>(P, sh, L.b_base, L.b_row, L.b_stride, L.tiles, L.n_whole, L.n_mixed, L.grads, L.packed,
-                             L.limit, L.flag, b, L.blocks);
-            return;
+        for (int p = 0; p < K; ++p) {
+            const PackLaunch& L = Z.k[p];
+            if (b < L.blocks) {
+                pack_body<CHECK>(P, sh, L.b_base, L.b_row, L.b_stride, L.tiles, L.n_whole, L.n_mixed, L.grads,
+                                 L.packed, L.limit, L.flag, b, L.blocks);
+                return;
+            }
+            b -= L.blocks;
         }
-        b -= L.blocks;
     }
 #pragma unroll
     for (int p = 0; p < K; ++p) {
@@ -69,13 +75,19 @@ template <int K>
 static void launch_z3(const zero_plan* plan, const ReduceLaunch* R, const PackLaunch* L, const UnpackLaunch* U,
                       bool check, int grid, hipStream_t s) {
     Z3Parts<K> Z{};  // absent parts: blocks == 0
-    for (int p = 0; p < K; ++p) Z.r[p] = R[p], Z.k[p] = L[p], Z.u[p] = U[p];
-    if (plan->dtype == ZERO_BF16) {
-        if (check) z3_kernel<ZERO_BF16, true, K><<<grid, kBlock, 0, s>>>(plan->dev, Z);
-        else z3_kernel<ZERO_BF16, false, K><<<grid, kBlock, 0, s>>>(plan->dev, Z);
+    bool gathers_only = true;
+    for (int p = 0; p < K; ++p) {
+        Z.r[p] = R[p], Z.k[p] = L[p], Z.u[p] = U[p];
+        gathers_only &= R[p].blocks == 0 && L[p].blocks == 0;
+    }
+    if (gathers_only) {  // the unpack body alone (a 16-bit copy: the data type does not matter)
+        z3_kernel<ZERO_BF16, false, K, 4><<<grid, kBlock, 0, s>>>(plan->dev, Z);
+    } else if (plan->dtype == ZERO_BF16) {
+        if (check) z3_kernel<ZERO_BF16, true, K, 7><<<grid, kBlock, 0, s>>>(plan->dev, Z);
+        else z3_kernel<ZERO_BF16, false, K, 7><<<grid, kBlock, 0, s>>>(plan->dev, Z);
     } else {
-        if (check) z3_kernel<ZERO_FP16, true, K><<<grid, kBlock, 0, s>>>(plan->dev, Z);
-        else z3_kernel<ZERO_FP16, false, K><<<grid, kBlock, 0, s>>>(plan->dev, Z);
+        if (check) z3_kernel<ZERO_FP16, true, K, 7><<<grid, kBlock, 0, s>>>(plan->dev, Z);
+        else z3_kernel<ZERO_FP16, false, K, 7><<<grid, kBlock, 0, s>>>(plan->dev, Z);
     }
 }
 
