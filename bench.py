@@ -713,7 +713,7 @@ KERNEL_KEYS = (("probe_adam_streams_kernel", "probe_adam_streams"), ("probe_copy
                ("unpack_kernel", "unpack"), ("pack_kernel", "pack"), ("reduce_kernel", "reduce"),
                ("adam_kernel", "adam"), ("overflow_kernel", "overflow"), ("shard_init_kernel", "shard_init"))
 SHORT_NAMES = tuple(s for _, s in KERNEL_KEYS) + ("pack_check",) + tuple(
-    f"z3 (up to {k} bucket{'s' if k != 1 else ''} per kind)" for k in (1, 2, 4))
+    f"z3{g} (up to {k} bucket{'s' if k != 1 else ''} per kind)" for k in (1, 2, 4) for g in ("", " gathers only"))
 
 
 def _short(name: str) -> str:
@@ -721,10 +721,13 @@ def _short(name: str) -> str:
         if key in name:
             if short == "pack" and ("true>" in name or "Lb1E" in name):
                 return "pack_check"  # the pack with the input check (fused path)
-            if short == "z3":  # the ZeRO-3 launch, by buckets per kind (template argument K)
+            if short == "z3":  # the ZeRO-3 launch, by buckets per kind (K) and kinds compiled in
                 k = (name.split("Z3Parts<")[1].split(">")[0] if "Z3Parts<" in name else
                      name.split("Z3PartsILi")[1].split("E")[0] if "Z3PartsILi" in name else "?")
-                return f"z3 (up to {k} bucket{'s' if k != '1' else ''} per kind)"
+                targs = name.split("z3_kernel<")[1].split(">")[0].replace(" ", "").split(",") if "z3_kernel<" in name \
+                    else []
+                kind = " gathers only" if targs[-1:] == ["4"] else ""
+                return f"z3{kind} (up to {k} bucket{'s' if k != '1' else ''} per kind)"
             return short
     return name[:60]
 
