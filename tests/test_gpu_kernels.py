@@ -149,6 +149,32 @@ def test_reduce_and_fused_flag(case, dtype):
     assert int(st.flag.item()) == oracle.overflow(pl, want, live)
 
 
+@pytest.mark.parametrize("nd", [15, 16, 17, 40])
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_reduce_row_forms_around_nd_16(nd, dtype):
+    """The reduce keeps two groups of rows in flight below Nd = 16 and one group on tiles inside
+    one parameter from Nd = 16; both sides of that switch, with partial last groups (Nd = 15, 17,
+    40) and whole tiles next to mixed ones, match the oracle bit for bit."""
+    rng = np.random.default_rng(nd)
+    numels = [nd * 2048 * 3 + 5, 7, nd * 2048 - 3, nd * 4096, 100003] + ragged_numels(rng, 30, nd, 90000)
+    st = Z.ShardStep(numels, nd, nd - 2, 0, dtype)
+    pl = oracle.plan(numels, nd, nd - 2, 0)
+    live = np.ones(len(numels), dtype=np.uint8)
+    live[1::4] = 0
+    st.live.copy_(torch.from_numpy(live))
+    st.g32.fill_(-7.0)
+    want = np.full(pl.shard_len, -7.0, dtype=np.float32)
+    for b in range(pl.n_buckets):
+        L = int(pl.buckets[b, oracle.B_STRIDE])
+        rows = special_rows(rng, nd, L + 8, dtype)
+        oracle.reduce_bucket(pl, b, np.ascontiguousarray(rows), dtype, live, want)
+        Z.zero_reduce_shard(st.plan, b, to_dev16(rows.reshape(-1)), L + 8, st.live, st.g32, st.flag)
+    torch.cuda.synchronize()
+    say(f"reduce row forms nd={nd} dtype={dtype} shard={pl.shard_len}")
+    assert_same_f32(to_np32(st.g32), want, "g32")
+    assert int(st.flag.item()) == oracle.overflow(pl, want, live)
+
+
 def test_reduce_exact_order_example():
     """Rows 1, 2^-24, 2^-24 must reduce to 1.0 (ascending order, seeded with rank 0)."""
     st = Z.ShardStep([3 * 64], 3, 0, 0, BF16)

@@ -106,23 +106,18 @@ __device__ __forceinline__ void adam_cols(const AdamK& K, const AdamArgs& A, int
     }
 }
 
-// A whole span of kBlock * COLS columns of one live parameter, lane-strided: in pass q the
-// block's threads take consecutive 4-column groups of the span's q-th kBlock * 4 columns, so
-// that every load and store instruction of a wavefront covers 1 KB (512 B for the 16-bit
-// parameters) of whole cache lines, and the loads can be nontemporal.  Measured on MI355X
-// against 8 consecutive columns per thread (two half-line instructions per array): 5-8%
-// faster on the 7.5B, GPT-2 and Llama lists; the layout alone, with ordinary loads, is level.
-__device__ __forceinline__ float4 load4f_nt(const float* p) {
-    const zs_f32x4 w = __builtin_nontemporal_load(gptr(reinterpret_cast<const zs_f32x4*>(p)));
-    return make_float4(w.x, w.y, w.z, w.w);
-}
+// A whole span of kBlock * COLS columns of one live parameter, lane-strided (see adam_quad):
+// every load and store instruction of a wavefront covers whole cache lines, so the loads can
+// be nontemporal.  Measured on MI355X against 8 consecutive columns per thread (two half-line
+// instructions per array): 5-8% faster on the 7.5B, GPT-2 and Llama lists; the layout alone,
+// with ordinary loads, is level.
 template <int DT, int COLS>
 __device__ __forceinline__ void adam_span(const AdamK& K, const AdamArgs& A, int64_t x0, float2 sc, uint16_t* lp0) {
     constexpr int V = COLS / 4;
     float4 g4[V], p4[V], m4[V], v4[V];
 #pragma unroll
     for (int q = 0; q < V; ++q) {
-        const int64_t x = x0 + int64_t(q) * kBlock * 4 + int64_t(threadIdx.x) * 4;
+        const int64_t x = x0 + quad_col(q);
         g4[q] = load4f_nt(A.g32 + x);
         p4[q] = load4f_nt(A.p32 + x);
         m4[q] = load4f_nt(A.m + x);
@@ -130,23 +125,8 @@ __device__ __forceinline__ void adam_span(const AdamK& K, const AdamArgs& A, int
     }
 #pragma unroll
     for (int q = 0; q < V; ++q) {
-        const int64_t xo = int64_t(q) * kBlock * 4 + int64_t(threadIdx.x) * 4;
-        float* gq = &g4[q].x;
-        float* pq = &p4[q].x;
-        float* mq = &m4[q].x;
-        float* vq = &v4[q].x;
-        uint16_t h[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            adam_elem(K, gq[t], pq[t], mq[t], vq[t], sc.x, sc.y);
-            h[t] = from_f32<DT>(pq[t]);
-        }
-        store4f(A.p32 + x0 + xo, p4[q]);
-        store4f(A.m + x0 + xo, m4[q]);
-        store4f(A.v + x0 + xo, v4[q]);
-        __builtin_nontemporal_store(
-            uint64_t(uint32_t(h[0]) | (uint32_t(h[1]) << 16)) | (uint64_t(uint32_t(h[2]) | (uint32_t(h[3]) << 16)) << 32),
-            gptr(reinterpret_cast<uint64_t*>(lp0 + xo)));
+        const int64_t xo = quad_col(q);
+        adam_quad<DT>(K, g4[q], p4[q], m4[q], v4[q], sc, A.p32 + x0 + xo, A.m + x0 + xo, A.v + x0 + xo, lp0 + xo);
     }
 }
 

@@ -7,20 +7,26 @@
 // It reads the 16 bytes of every rank's row at those columns (aligned dwordx4: rows start on
 // 16-byte boundaries), converts exactly to fp32 and adds in ascending rank order, seeded with
 // rank 0's value — the fixed order that makes the sums bit-reproducible.  The rows are read
-// in groups of eight, and the next group's loads are issued before the current group's adds,
-// so HBM latency overlaps the arithmetic.
+// in groups of eight with nontemporal loads.  Below Nd = 16 the next group's loads are issued
+// before the current group's adds (two groups in flight); from Nd = 16 a tile inside one
+// parameter keeps one group in flight, which measured on MI355X 0.4-9% faster than two at every
+// Nd from 16 to 128 on the GPT-2 and 7.5B lists (the two-group form's extra registers cost
+// occupancy), and 3-5% slower at Nd = 8.  Tiles holding several parameters keep two groups.
 // Columns of parameters without a gradient are skipped before any row is read.  The overflow
 // flag is ORed once per wavefront (a ballot, then one atomic), only when a value is found.
 #include "zs_reduce.h"
 
 namespace zs {
 
-template <int DT>
+// Nd from which whole tiles keep one group of rows in flight (kRowsGroup) instead of two.
+constexpr int64_t kGroupFormNd = 16;
+
+template <int DT, int WHOLE>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_base, int64_t b_row, int64_t tile0,
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
-    reduce_body<DT, true, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
+    reduce_body<DT, WHOLE, kRowsPipe, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,
@@ -74,12 +80,11 @@ extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const
         L.blocks == 0)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    if (plan->dtype == ZERO_BF16)
-        reduce_kernel<ZERO_BF16><<<int(L.blocks), kBlock, 0, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile,
-                                                                  L.rows, L.row_stride, L.live, L.g32, L.flag);
-    else
-        reduce_kernel<ZERO_FP16><<<int(L.blocks), kBlock, 0, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile,
-                                                                  L.rows, L.row_stride, L.live, L.g32, L.flag);
+    const bool group = plan->nd >= kGroupFormNd;
+    auto kern = plan->dtype == ZERO_BF16 ? (group ? reduce_kernel<ZERO_BF16, kRowsGroup> : reduce_kernel<ZERO_BF16, kRowsPipe>)
+                                         : (group ? reduce_kernel<ZERO_FP16, kRowsGroup> : reduce_kernel<ZERO_FP16, kRowsPipe>);
+    kern<<<int(L.blocks), kBlock, 0, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile, L.rows, L.row_stride, L.live,
+                                          L.g32, L.flag);
     return check_launch("zero_reduce_shard");
 }
 

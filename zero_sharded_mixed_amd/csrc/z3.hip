@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kBlock) void z3_kernel(DevPlan P, Z3Parts<K> Z) {
         for (int p = 0; p < K; ++p) {
             const ReduceLaunch& R = Z.r[p];
             if (b < R.blocks) {
-                reduce_body<DT, false, false>(P, R.b_base, R.b_row, R.tile0, R.n_tile, R.rows, R.row_stride, R.live,
+                reduce_body<DT, kRowsLow, kRowsLow, false>(P, R.b_base, R.b_row, R.tile0, R.n_tile, R.rows, R.row_stride, R.live,
                                               R.g32, R.flag, b, R.blocks);
                 return;
             }

@@ -45,4 +45,33 @@ __device__ __forceinline__ void adam_elem(const AdamK& K, float g32, float& p, f
     p = __builtin_fmaf(-step_size, m / denom, p);
 }
 
+// Lane-strided layout of a span of columns: in pass q the block's threads take consecutive
+// 4-column groups of the span's q-th kBlock * 4 columns, so that every load and store
+// instruction of a wavefront covers 1 KB of fp32 (512 B of the 16-bit parameters) of whole
+// cache lines.  quad_col(q) is the thread's first column in pass q, relative to the span.
+__device__ __forceinline__ int64_t quad_col(int q) { return int64_t(q) * kBlock * 4 + int64_t(threadIdx.x) * 4; }
+
+// The update of 4 consecutive columns of one parameter from g (the reduced gradient) and the
+// loaded p, m, v: stores p, m, v at p32, m, v and the four new 16-bit parameters at lp.
+template <int DT>
+__device__ __forceinline__ void adam_quad(const AdamK& K, const float4& g, float4 p, float4 m, float4 v, float2 sc,
+                                          float* p32, float* mm, float* vv, uint16_t* lp) {
+    const float* gq = &g.x;
+    float* pq = &p.x;
+    float* mq = &m.x;
+    float* vq = &v.x;
+    uint16_t h[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        adam_elem(K, gq[t], pq[t], mq[t], vq[t], sc.x, sc.y);
+        h[t] = from_f32<DT>(pq[t]);
+    }
+    store4f(p32, p);
+    store4f(mm, m);
+    store4f(vv, v);
+    __builtin_nontemporal_store(
+        uint64_t(uint32_t(h[0]) | (uint32_t(h[1]) << 16)) | (uint64_t(uint32_t(h[2]) | (uint32_t(h[3]) << 16)) << 32),
+        gptr(reinterpret_cast<uint64_t*>(lp)));
+}
+
 }  // namespace zs

@@ -135,6 +135,10 @@ __device__ __forceinline__ void store4f(float* p, const float4& v) {
     zs_f32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, gptr(reinterpret_cast<zs_f32x4*>(p)));
 }
+__device__ __forceinline__ float4 load4f_nt(const float* p) {
+    const zs_f32x4 w = __builtin_nontemporal_load(gptr(reinterpret_cast<const zs_f32x4*>(p)));
+    return make_float4(w.x, w.y, w.z, w.w);
+}
 
 // Sixteen bytes from any 2-byte aligned address: one global_load_dwordx4, the memory system
 // handling the misalignment (measured on MI355X: unaligned 16-byte loads of a streaming copy
@@ -213,16 +217,19 @@ __device__ __forceinline__ bool non_finite(float f) { return (__float_as_uint(f)
 // Eight columns of the rank rows: acc = f32(row_0), then acc = acc + f32(row_k) for
 // k = 1..nd-1 (one fp32 round-to-nearest-even addition each, in this order).  The columns are
 // element `lane` of row k starting at rows_u + k * row_stride, rows_u uniform across the
-// wavefront (the tile's first column) and lane the thread's offset in the tile.  The rows are
-// loaded in groups of kAhead, each group whole before its adds.  With PIPE, groups start at row
-// 0, the next group's loads go out before the current group's adds (a thread always has a group
-// in flight) and the last partial group is loaded whole: measured on MI355X 1-4% faster in a
-// reduce of its own, but the two groups in registers take 160 VGPRs, which a kernel that shares
-// its registers with the pack and the unpack cannot afford (the ZeRO-3 layer launch lost 5%).
-// Without PIPE: row 0, then groups from row 1, then the rest one row at a time.  NT makes the
-// row loads nontemporal (each wave's load covers 1 KB of whole lines): 0.5-3.4% faster in the
-// reduce of its own on all four lists; in the fused reduce + Adam, which also streams p32, m
-// and v, 3% slower at Nd = 64, so it is the reduce's alone.
+// wavefront (the tile's first column) and lane the thread's offset in the tile.  Every form
+// adds in the same order; they differ in how many row loads a thread keeps in flight, which
+// sets its registers, and the kernels pick the form that measured fastest for them on MI355X:
+//   kRowsLow   row 0, then groups of kAhead rows from row 1, then one row at a time: fewest
+//              registers (the ZeRO-3 layer launch, which shares its registers with the pack
+//              and the unpack, and the fused reduce + Adam on whole tiles);
+//   kRowsGroup groups of kAhead rows from row 0, each group's loads then its adds, the last
+//              partial group loaded whole (the reduce's whole tiles at Nd >= 16);
+//   kRowsPipe  the same groups with the next group's loads issued before the current group's
+//              adds, two groups in registers (the reduce at Nd < 16, the reduce's and the fused
+//              kernel's tiles that hold several parameters).
+// NT makes the row loads nontemporal (each wave's load covers 1 KB of whole lines).
+enum RowForm { kRowsLow, kRowsGroup, kRowsPipe };
 constexpr int kAhead = 8;
 template <int DT>
 __device__ __forceinline__ void reduce_group_adds(float (&acc)[8], const uint4 (&v)[kAhead], bool first) {
@@ -237,13 +244,27 @@ __device__ __forceinline__ void reduce_group_loads(uint4 (&v)[kAhead], const uin
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) v[u] = load16_off<NT>(rows_u + (k + u) * row_stride, lane_bytes);
 }
-template <int DT, bool PIPE, bool NT = false>
+template <int DT, int FORM, bool NT = false>
 __device__ __forceinline__ void reduce_rows8(const uint16_t* rows_u, uint32_t lane, int64_t nd, int64_t row_stride,
                                              float (&acc)[8]) {
     const uint32_t lb = lane * 2u;
     const int64_t ng = nd / kAhead;  // full groups
     uint4 a[kAhead];
-    if constexpr (PIPE) {
+    if constexpr (FORM == kRowsLow) {
+        accumulate8<DT, true>(acc, load16_off<NT>(rows_u, lb));
+        int64_t k = 1;
+        for (; k + kAhead <= nd; k += kAhead) {
+            reduce_group_loads<NT>(a, rows_u, lb, k, row_stride);
+            reduce_group_adds<DT>(acc, a, false);
+        }
+        for (; k < nd; ++k) accumulate8<DT, false>(acc, load16_off<NT>(rows_u + k * row_stride, lb));
+        return;
+    } else if constexpr (FORM == kRowsGroup) {
+        for (int64_t g = 0; g < ng; ++g) {
+            reduce_group_loads<NT>(a, rows_u, lb, g * kAhead, row_stride);
+            reduce_group_adds<DT>(acc, a, g == 0);
+        }
+    } else {
         uint4 b[kAhead];
         if (ng > 0) {
             reduce_group_loads<NT>(a, rows_u, lb, 0, row_stride);
@@ -256,16 +277,6 @@ __device__ __forceinline__ void reduce_rows8(const uint16_t* rows_u, uint32_t la
                 if (g + 2 >= ng) break;
             }
         }
-    } else {
-        // fewest registers: row 0, then groups of kAhead rows from row 1, then one row at a time
-        accumulate8<DT, true>(acc, load16_off<NT>(rows_u, lb));
-        int64_t k = 1;
-        for (; k + kAhead <= nd; k += kAhead) {
-            reduce_group_loads<NT>(a, rows_u, lb, k, row_stride);
-            reduce_group_adds<DT>(acc, a, false);
-        }
-        for (; k < nd; ++k) accumulate8<DT, false>(acc, load16_off<NT>(rows_u + k * row_stride, lb));
-        return;
     }
     const int rem = int(nd - ng * kAhead);
     if (rem == 0) return;

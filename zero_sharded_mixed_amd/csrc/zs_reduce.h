@@ -12,11 +12,11 @@ namespace zs {
 constexpr int kReduceTiles = ZS_REDUCE_TILES;  // consecutive tiles per block (one chunk of each per thread)
 
 // x: the thread's first column; rows_u: the rows at the tile's first column (uniform)
-template <int DT, bool PIPE, bool NT>
+template <int DT, int FORM, bool NT>
 __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, unsigned mask, const uint16_t* rows_u,
                                              int64_t row_stride, float* __restrict__ g32, bool& bad) {
     float acc[8];
-    reduce_rows8<DT, PIPE, NT>(rows_u, threadIdx.x * kChunk, P.nd, row_stride, acc);
+    reduce_rows8<DT, FORM, NT>(rows_u, threadIdx.x * kChunk, P.nd, row_stride, acc);
     float* dst = g32 + x;
     if (mask == 0xffu) {
         store4f(dst, make_float4(acc[0], acc[1], acc[2], acc[3]));
@@ -29,8 +29,9 @@ __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, unsign
     bad |= any_bad8(acc, mask);
 }
 
-// PIPE, NT: see reduce_rows8 (a launch of its own uses both; the ZeRO-3 layer launch neither).
-template <int DT, bool PIPE, bool NT>
+// WHOLE, MIXED: the row forms of reduce_rows8 for tiles inside one parameter and for the other
+// tiles; NT: nontemporal row loads (a launch of its own uses them, the ZeRO-3 layer launch not).
+template <int DT, int WHOLE, int MIXED, bool NT>
 __device__ __forceinline__ void reduce_body(const DevPlan& P, int64_t b_base, int64_t b_row, int64_t tile0,
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
@@ -56,7 +57,10 @@ __device__ __forceinline__ void reduce_body(const DevPlan& P, int64_t b_base, in
             if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
             const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
             if (mask == 0) continue;
-            reduce_chunk<DT, PIPE, NT>(P, x, mask, rows + (x0 + t * kTileCols - b_base), row_stride, g32, bad);
+            const uint16_t* rows_u = rows + (x0 + t * kTileCols - b_base);
+            if constexpr (WHOLE == MIXED) reduce_chunk<DT, WHOLE, NT>(P, x, mask, rows_u, row_stride, g32, bad);
+            else if (whole) reduce_chunk<DT, WHOLE, NT>(P, x, mask, rows_u, row_stride, g32, bad);
+            else reduce_chunk<DT, MIXED, NT>(P, x, mask, rows_u, row_stride, g32, bad);
         }
     }
     if (flag) flag_wave(bad, flag);
