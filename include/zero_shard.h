@@ -326,8 +326,9 @@ zero_status zero_adam_step_noalloc(const zero_plan* plan, const float* d_g32, fl
                                    const int32_t* d_flag, void* d_arena, void* stream);
 
 /* ------------------------------------------- fused path: reduce + check + Adam ------ */
-/* The same step with the reduced gradient kept in registers: the sum of the Nd rows goes
- * straight into the Adam update, so the fp32 gradient shard is neither written nor read.
+/* The same step with the reduced gradient kept on chip (in registers, or in the block's LDS
+ * for a tile inside one parameter): the sum of the Nd rows goes straight into the Adam update,
+ * so the fp32 gradient shard is neither written nor read.
  * Because the step must be skipped before any state changes, the overflow verdict comes
  * from the inputs rather than from the sums.  Per step, on one stream:
  *   1. *d_flag = 0; zero_pack_bucket_check for every bucket (this rank's gradients);
