@@ -84,8 +84,10 @@ __global__ __launch_bounds__(kBlock) void reduce_adam_kernel(DevPlan P, int64_t 
         if (mask == 0) continue;
         const bool one_param = i < P.n && P.off[i] <= x && x + kChunk <= P.end[i];
         const bool vec = mask == 0xffu && one_param;
+        // the other tiles: two groups of rows in flight, nontemporal row loads (2.5% faster on
+        // the ragged list, where these tiles dominate; level on the model lists)
         float acc[8];
-        reduce_rows8<DT, kRowsPipe>(rows + (x0 - b_base), threadIdx.x * kChunk, P.nd, row_stride, acc);
+        reduce_rows8<DT, kRowsPipe, true>(rows + (x0 - b_base), threadIdx.x * kChunk, P.nd, row_stride, acc);
         if (vec) {
             // eight columns of one live parameter: two 4-column updates
             const float2 sc = scal[i];
