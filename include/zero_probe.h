@@ -9,8 +9,9 @@
  *
  * Every probe launches a one-shot grid (one block of 256 threads per 4 KiB of the first
  * stream, one 16-byte chunk per thread per stream, like the pipeline kernels; every
- * wavefront instruction covering whole cache lines, all loads and stores nontemporal: the
- * fastest form of each pattern on MI355X) on `stream`,
+ * wavefront instruction covering whole cache lines, all loads and stores nontemporal; the
+ * write and the Adam-mix probes with their blocks per CU capped at four and two through an
+ * LDS reservation: the fastest form of each pattern on MI355X) on `stream`,
  * never allocates and never synchronises.  Sizes are in bytes (multiples of 16) or elements
  * (multiples of 8).  Buffers are caller-owned device memory, 16-byte aligned, and must stay
  * allocated until the launched work has finished.  Every call returns ZERO_OK, ZERO_EINVAL

@@ -61,85 +61,43 @@ struct AdamArgs {
     uint16_t* arena;
 };
 
-#ifndef ZS_ADAM_COLS
-#define ZS_ADAM_COLS 8
-#endif
-constexpr int kAdamCols = ZS_ADAM_COLS;  // shard columns per thread (4 or 8)
+constexpr int kAdamCols = 8;  // shard columns per thread
+constexpr int64_t kSpan = int64_t(kBlock) * kAdamCols;  // shard columns per block
+static_assert(kSpan == kTileCols, "a span is one shard tile");
 
-// COLS consecutive columns of one live parameter: COLS/4 dwordx4 loads each of g, p, m, v;
-// COLS/4 dwordx4 stores each of p, m, v; one store of the COLS 16-bit parameters.
-template <int DT, int COLS>
-__device__ __forceinline__ void adam_cols(const AdamK& K, const AdamArgs& A, int64_t x, float2 sc, uint16_t* lp_dst) {
-    constexpr int V = COLS / 4;
-    float4 g4[V], p4[V], m4[V], v4[V];
+// Two 4-column groups of one live parameter, at shard columns xa and xb (lpa, lpb: their
+// 16-bit parameters in the all-gather block): the loads of both groups, then both updates.
+// NT: nontemporal loads, for groups laid out so that each wave's loads cover whole lines.
+template <int DT, bool NT>
+__device__ __forceinline__ void adam_two_quads(const AdamK& K, const AdamArgs& A, int64_t xa, int64_t xb, float2 sc,
+                                               uint16_t* lpa, uint16_t* lpb) {
+    const int64_t xs[2] = {xa, xb};
+    float4 g4[2], p4[2], m4[2], v4[2];
 #pragma unroll
-    for (int q = 0; q < V; ++q) {
-        g4[q] = load4f(A.g32 + x + 4 * q);
-        p4[q] = load4f(A.p32 + x + 4 * q);
-        m4[q] = load4f(A.m + x + 4 * q);
-        v4[q] = load4f(A.v + x + 4 * q);
+    for (int q = 0; q < 2; ++q) {
+        const int64_t x = xs[q];
+        g4[q] = NT ? load4f_nt(A.g32 + x) : load4f(A.g32 + x);
+        p4[q] = NT ? load4f_nt(A.p32 + x) : load4f(A.p32 + x);
+        m4[q] = NT ? load4f_nt(A.m + x) : load4f(A.m + x);
+        v4[q] = NT ? load4f_nt(A.v + x) : load4f(A.v + x);
     }
-    uint16_t h[COLS];
-#pragma unroll
-    for (int q = 0; q < V; ++q) {
-        float* gq = &g4[q].x;
-        float* pq = &p4[q].x;
-        float* mq = &m4[q].x;
-        float* vq = &v4[q].x;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            adam_elem(K, gq[t], pq[t], mq[t], vq[t], sc.x, sc.y);
-            h[4 * q + t] = from_f32<DT>(pq[t]);
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < V; ++q) {
-        store4f(A.p32 + x + 4 * q, p4[q]);
-        store4f(A.m + x + 4 * q, m4[q]);
-        store4f(A.v + x + 4 * q, v4[q]);
-    }
-    if constexpr (COLS == 8) {
-        store16(lp_dst, pack8(h));
-    } else {
-        *gptr(reinterpret_cast<uint64_t*>(lp_dst)) =
-            uint64_t(uint32_t(h[0]) | (uint32_t(h[1]) << 16)) | (uint64_t(uint32_t(h[2]) | (uint32_t(h[3]) << 16)) << 32);
-    }
+    adam_quad<DT>(K, g4[0], p4[0], m4[0], v4[0], sc, A.p32 + xa, A.m + xa, A.v + xa, lpa);
+    adam_quad<DT>(K, g4[1], p4[1], m4[1], v4[1], sc, A.p32 + xb, A.m + xb, A.v + xb, lpb);
 }
 
-// A whole span of kBlock * COLS columns of one live parameter, lane-strided (see adam_quad):
-// every load and store instruction of a wavefront covers whole cache lines, so the loads can
-// be nontemporal.  Measured on MI355X against 8 consecutive columns per thread (two half-line
-// instructions per array): 5-8% faster on the 7.5B, GPT-2 and Llama lists; the layout alone,
-// with ordinary loads, is level.
-template <int DT, int COLS>
-__device__ __forceinline__ void adam_span(const AdamK& K, const AdamArgs& A, int64_t x0, float2 sc, uint16_t* lp0) {
-    constexpr int V = COLS / 4;
-    float4 g4[V], p4[V], m4[V], v4[V];
-#pragma unroll
-    for (int q = 0; q < V; ++q) {
-        const int64_t x = x0 + quad_col(q);
-        g4[q] = load4f_nt(A.g32 + x);
-        p4[q] = load4f_nt(A.p32 + x);
-        m4[q] = load4f_nt(A.m + x);
-        v4[q] = load4f_nt(A.v + x);
-    }
-#pragma unroll
-    for (int q = 0; q < V; ++q) {
-        const int64_t xo = quad_col(q);
-        adam_quad<DT>(K, g4[q], p4[q], m4[q], v4[q], sc, A.p32 + x0 + xo, A.m + x0 + xo, A.v + x0 + xo, lp0 + xo);
-    }
-}
-
-// One block per span of kBlock * COLS shard columns.
-template <int DT, int COLS>
+// One block per span of kSpan shard columns.  A span inside one live parameter is taken
+// lane-strided (quad_col): every load and store instruction of a wavefront covers whole cache
+// lines, so the loads can be nontemporal.  Measured on MI355X against 8 consecutive columns
+// per thread (two half-line instructions per array): 5-8% faster on the 7.5B, GPT-2 and Llama
+// lists; the layout alone, with ordinary loads, is level.  Other spans go 8 consecutive
+// columns per thread, element by element where parameters, dead slots or a row gap meet.
+template <int DT>
 __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int64_t n_spans) {
     if (A.flag && *A.flag) return;
-    constexpr int64_t kSpan = int64_t(kBlock) * COLS;
-    static_assert(kTileCols % kSpan == 0, "a span never crosses a tile");
     const AdamK K = load_adam_consts(A.consts);
     for (int64_t sp = blockIdx.x; sp < n_spans; sp += gridDim.x) {
         const int64_t x0 = sp * kSpan;
-        const int64_t x = x0 + int64_t(threadIdx.x) * COLS;
+        const int64_t x = x0 + int64_t(threadIdx.x) * kAdamCols;
         // block-uniform (scalar loads): the whole span inside one parameter -> its scalars
         const int64_t iu = ld_const(P.tile_first, x0 >> kTileShift);
         const int64_t ic = iu < P.n ? iu : P.n - 1;
@@ -150,24 +108,27 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(DevPlan P, AdamArgs A, int
         if (iu < P.n && off <= x0 && end >= x0 + kSpan) {
             if (!lv) continue;
             const int64_t O = ld_const(P.b_base, bu);
-            adam_span<DT, COLS>(K, A, x0, sc, A.arena + P.nd * O + P.rank * ld_const(P.b_stride, bu) + (x0 - O));
+            uint16_t* lp0 = A.arena + P.nd * O + P.rank * ld_const(P.b_stride, bu) + (x0 - O);
+            adam_two_quads<DT, true>(K, A, x0 + quad_col(0), x0 + quad_col(1), sc, lp0 + quad_col(0),
+                                     lp0 + quad_col(1));
             continue;
         }
         if (x >= P.shard_numel) continue;
         int64_t i = param_of_column(P, x);
-        if (i < P.n && P.off[i] <= x && x + COLS <= P.end[i]) {
+        if (i < P.n && P.off[i] <= x && x + kAdamCols <= P.end[i]) {
             // the thread's columns inside parameter i
             if (!A.live[i]) continue;
             const int32_t b = P.bucket[i];
             const int64_t O = P.b_base[b];
-            adam_cols<DT, COLS>(K, A, x, A.scal[i], A.arena + P.nd * O + P.rank * P.b_stride[b] + (x - O));
+            uint16_t* lp = A.arena + P.nd * O + P.rank * P.b_stride[b] + (x - O);
+            adam_two_quads<DT, false>(K, A, x, x + 4, A.scal[i], lp, lp + 4);
         } else {
             // columns across parameters, dead slots or a row gap: element by element
             ZS_GLOBAL float* p32 = gptr(A.p32);
             ZS_GLOBAL float* mm = gptr(A.m);
             ZS_GLOBAL float* vv = gptr(A.v);
 #pragma unroll
-            for (int t = 0; t < COLS; ++t) {
+            for (int t = 0; t < kAdamCols; ++t) {
                 const int64_t xt = x + t;
                 while (i < P.n && P.end[i] <= xt) ++i;
                 if (!(i < P.n && P.off[i] <= xt) || !A.live[i]) continue;
@@ -230,13 +191,12 @@ static zero_status adam_step_with(const zero_plan* plan, const float* d_g32, flo
     if (st != ZERO_OK) return st;
     if (plan->shard_numel == 0) return ZERO_OK;
     AdamArgs A{d_g32, d_p32, d_m, d_v, d_live, scal, consts, d_flag, static_cast<uint16_t*>(d_arena)};
-    const int64_t span = int64_t(kBlock) * kAdamCols;
-    const int64_t n_spans = (plan->shard_numel + span - 1) / span;
+    const int64_t n_spans = (plan->shard_numel + kSpan - 1) / kSpan;
     const int g = grid_for(n_spans);
     if (plan->dtype == ZERO_BF16)
-        adam_kernel<ZERO_BF16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
+        adam_kernel<ZERO_BF16><<<g, kBlock, kTwoBlocksLds, s>>>(plan->dev, A, n_spans);
     else
-        adam_kernel<ZERO_FP16, kAdamCols><<<g, kBlock, 0, s>>>(plan->dev, A, n_spans);
+        adam_kernel<ZERO_FP16><<<g, kBlock, kTwoBlocksLds, s>>>(plan->dev, A, n_spans);
     return check_launch(who);
 }
 }  // namespace zs

@@ -9,9 +9,9 @@
 // rank 0's value — the fixed order that makes the sums bit-reproducible.  The rows are read
 // in groups of eight with nontemporal loads.  Below Nd = 16 the next group's loads are issued
 // before the current group's adds (two groups in flight); from Nd = 16 a tile inside one
-// parameter keeps one group in flight, which measured on MI355X 0.4-9% faster than two at every
-// Nd from 16 to 128 on the GPT-2 and 7.5B lists (the two-group form's extra registers cost
-// occupancy), and 3-5% slower at Nd = 8.  Tiles holding several parameters keep two groups.
+// parameter keeps one group in flight, at two blocks per CU: measured on MI355X 0.4-9% faster
+// than two groups at every Nd from 16 to 128 on the GPT-2 and 7.5B lists, and 3-5% slower at
+// Nd = 8.  Tiles holding several parameters keep two groups.
 // Columns of parameters without a gradient are skipped before any row is read.  The overflow
 // flag is ORed once per wavefront (a ballot, then one atomic), only when a value is found.
 #include "zs_reduce.h"
@@ -83,8 +83,9 @@ extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const
     const bool group = plan->nd >= kGroupFormNd;
     auto kern = plan->dtype == ZERO_BF16 ? (group ? reduce_kernel<ZERO_BF16, kRowsGroup> : reduce_kernel<ZERO_BF16, kRowsPipe>)
                                          : (group ? reduce_kernel<ZERO_FP16, kRowsGroup> : reduce_kernel<ZERO_FP16, kRowsPipe>);
-    kern<<<int(L.blocks), kBlock, 0, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile, L.rows, L.row_stride, L.live,
-                                          L.g32, L.flag);
+    // the one-group form runs at two blocks per CU (kTwoBlocksLds), the two-group form uncapped
+    kern<<<int(L.blocks), kBlock, group ? kTwoBlocksLds : 0u, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile,
+                                                                    L.rows, L.row_stride, L.live, L.g32, L.flag);
     return check_launch("zero_reduce_shard");
 }
 

@@ -7,10 +7,7 @@
 namespace zs {
 
 // ------------------------------------------------------------------------------- pack --
-#ifndef ZS_UNPACK_UNROLL
-#define ZS_UNPACK_UNROLL 2
-#endif
-constexpr int kUnpackUnroll = ZS_UNPACK_UNROLL;  // chunks per thread per iteration of the unpack
+constexpr int kUnpackUnroll = 2;  // chunks per thread per iteration of the unpack
 
 
 // The input check of the checked pack: true if one of the eight 16-bit values is inf or NaN
@@ -110,10 +107,7 @@ __device__ __forceinline__ void pack_chunk_generic(const DevPlan& P, int64_t i, 
 
 // Mixed tiles stage the parameters that overlap them in LDS (at most kStageMax; tiles touching
 // more parameters go chunk by chunk through the generic path).
-#ifndef ZS_STAGE_MAX
-#define ZS_STAGE_MAX 256
-#endif
-constexpr int kStageMax = ZS_STAGE_MAX;
+constexpr int kStageMax = 256;
 
 // Work items of one bucket, in dispatch order:
 //  * mixed tiles (several parameters, padding, the row gap): kMixRows rows of one tile per
@@ -131,15 +125,9 @@ constexpr int kStageMax = ZS_STAGE_MAX;
 // block are 1% slower than 8 on the ragged list, 16 rows up to 50% slower (the run's 16 loads in
 // flight cost registers, hence occupancy).
 // tiles: the bucket's n_whole whole tiles, then its n_mixed mixed tiles (plan tables).
-#ifndef ZS_MIX_ROWS
-#define ZS_MIX_ROWS 8
-#endif
-#ifndef ZS_WHOLE_ROWS
-#define ZS_WHOLE_ROWS 2
-#endif
-constexpr int kMixRows = ZS_MIX_ROWS;        // rows per block of a mixed tile
+constexpr int kMixRows = 8;       // rows per block of a mixed tile
 static_assert(kMixRows >= 1 && kMixRows < 32, "a run's rows are a 32-bit mask");
-constexpr int kWholeRows = ZS_WHOLE_ROWS;    // rows per block of a whole tile
+constexpr int kWholeRows = 2;   // rows per block of a whole tile
 
 // The fields a whole-tile work item needs: its rows, its columns' parameter and that
 // parameter's gradient pointer (NULL = no gradient this step).

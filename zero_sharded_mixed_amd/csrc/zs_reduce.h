@@ -6,11 +6,6 @@
 
 namespace zs {
 
-#ifndef ZS_REDUCE_TILES
-#define ZS_REDUCE_TILES 1
-#endif
-constexpr int kReduceTiles = ZS_REDUCE_TILES;  // consecutive tiles per block (one chunk of each per thread)
-
 // x: the thread's first column; rows_u: the rows at the tile's first column (uniform)
 template <int DT, int FORM, bool NT>
 __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, unsigned mask, const uint16_t* rows_u,
@@ -33,41 +28,36 @@ __device__ __forceinline__ void reduce_chunk(const DevPlan& P, int64_t x, unsign
 // tiles; NT: nontemporal row loads (a launch of its own uses them, the ZeRO-3 layer launch not).
 template <int DT, int WHOLE, int MIXED, bool NT>
 __device__ __forceinline__ void reduce_body(const DevPlan& P, int64_t b_base, int64_t b_row, int64_t tile0,
-                                                        int64_t n_tile, const uint16_t* __restrict__ rows,
-                                                        int64_t row_stride, const uint8_t* __restrict__ live,
-                                                        float* __restrict__ g32, int32_t* __restrict__ flag,
-                                            int64_t vbid, int64_t vgrid) {
-    const int64_t n_groups = (n_tile + kReduceTiles - 1) / kReduceTiles;
+                                            int64_t n_tile, const uint16_t* __restrict__ rows, int64_t row_stride,
+                                            const uint8_t* __restrict__ live, float* __restrict__ g32,
+                                            int32_t* __restrict__ flag, int64_t vbid, int64_t vgrid) {
     bool bad = false;
-    for (int64_t w = vbid; w < n_groups; w += vgrid) {
-        const int64_t j = tile0 + w * kReduceTiles;
+    for (int64_t w = vbid; w < n_tile; w += vgrid) {
+        const int64_t j = tile0 + w;
         const int64_t x0 = j << kTileShift;
-        // block-uniform (scalar loads): does the whole group of tiles lie inside one parameter,
-        // hence inside this bucket, and is that parameter live?
+        // block-uniform (scalar loads): does the tile lie inside one parameter, hence inside
+        // this bucket, and is that parameter live?
         const int64_t iu = ld_const(P.tile_first, j);
         const int64_t ic = iu < P.n ? iu : P.n - 1;
         const int64_t off = ld_const(P.off, ic), end = ld_const(P.end, ic);
         const bool lv = ld_const(live, ic) != 0;
-        const bool whole = iu < P.n && off <= x0 && end >= x0 + kReduceTiles * kTileCols;
+        const bool whole = iu < P.n && off <= x0 && end >= x0 + kTileCols;
         if (whole && !lv) continue;
-#pragma unroll
-        for (int t = 0; t < kReduceTiles; ++t) {
-            const int64_t x = x0 + t * kTileCols + int64_t(threadIdx.x) * kChunk;
-            const int64_t c = x - b_base;
-            if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
-            const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
-            if (mask == 0) continue;
-            const uint16_t* rows_u = rows + (x0 + t * kTileCols - b_base);
-            if constexpr (WHOLE == MIXED) reduce_chunk<DT, WHOLE, NT>(P, x, mask, rows_u, row_stride, g32, bad);
-            else if (whole) reduce_chunk<DT, WHOLE, NT>(P, x, mask, rows_u, row_stride, g32, bad);
-            else reduce_chunk<DT, MIXED, NT>(P, x, mask, rows_u, row_stride, g32, bad);
-        }
+        const int64_t x = x0 + int64_t(threadIdx.x) * kChunk;
+        const int64_t c = x - b_base;
+        if (!whole && (c < 0 || c >= b_row)) continue;  // outside the bucket, or entirely in the row gap
+        const unsigned mask = whole ? 0xffu : live_mask8(P, live, x, param_of_column(P, x));
+        if (mask == 0) continue;
+        const uint16_t* rows_u = rows + (x0 - b_base);
+        if constexpr (WHOLE == MIXED) reduce_chunk<DT, WHOLE, NT>(P, x, mask, rows_u, row_stride, g32, bad);
+        else if (whole) reduce_chunk<DT, WHOLE, NT>(P, x, mask, rows_u, row_stride, g32, bad);
+        else reduce_chunk<DT, MIXED, NT>(P, x, mask, rows_u, row_stride, g32, bad);
     }
     if (flag) flag_wave(bad, flag);
 }
 
-// Number of virtual blocks the reduce of n_tile tiles uses.
-inline int64_t reduce_blocks(int64_t n_tile) { return grid_for((n_tile + kReduceTiles - 1) / kReduceTiles); }
+// Number of virtual blocks the reduce of n_tile tiles uses (one per tile, up to the grid cap).
+inline int64_t reduce_blocks(int64_t n_tile) { return grid_for(n_tile); }
 
 // A validated reduce of one bucket, ready to run, and its block count (0 = nothing to do).
 struct ReduceLaunch {
