@@ -152,9 +152,10 @@ def test_reduce_and_fused_flag(case, dtype):
 @pytest.mark.parametrize("nd", [15, 16, 17, 40])
 @pytest.mark.parametrize("dtype", [BF16, FP16])
 def test_reduce_row_forms_around_nd_16(nd, dtype):
-    """The reduce keeps two groups of rows in flight below Nd = 16 and one group on tiles inside
-    one parameter from Nd = 16; both sides of that switch, with partial last groups (Nd = 15, 17,
-    40) and whole tiles next to mixed ones, match the oracle bit for bit."""
+    """The reduce runs one kernel below Nd = 16 (one group of rows in flight on every tile) and
+    another from Nd = 16 (one group on tiles inside one parameter, two on the others); both sides
+    of that switch, with partial last groups (Nd = 15, 17, 40) and whole tiles next to mixed ones,
+    match the oracle bit for bit."""
     rng = np.random.default_rng(nd)
     numels = [nd * 2048 * 3 + 5, 7, nd * 2048 - 3, nd * 4096, 100003] + ragged_numels(rng, 30, nd, 90000)
     st = Z.ShardStep(numels, nd, nd - 2, 0, dtype)

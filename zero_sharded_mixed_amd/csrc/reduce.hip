@@ -7,26 +7,29 @@
 // It reads the 16 bytes of every rank's row at those columns (aligned dwordx4: rows start on
 // 16-byte boundaries), converts exactly to fp32 and adds in ascending rank order, seeded with
 // rank 0's value — the fixed order that makes the sums bit-reproducible.  The rows are read
-// in groups of eight with nontemporal loads.  Below Nd = 16 the next group's loads are issued
-// before the current group's adds (two groups in flight); from Nd = 16 a tile inside one
-// parameter keeps one group in flight, at two blocks per CU: measured on MI355X 0.4-9% faster
-// than two groups at every Nd from 16 to 128 on the GPT-2 and 7.5B lists, and 3-5% slower at
-// Nd = 8.  Tiles holding several parameters keep two groups.
+// in groups of eight with nontemporal loads, each group's loads before its adds.  Two kernels,
+// chosen by Nd, measured on MI355X against each other and against two groups in flight:
+//   * Nd >= 16: a tile inside one parameter keeps one group in flight and the others two (the
+//     ragged list's mixed tiles: 4% faster than one), at two blocks per CU: 0.4-9% faster than
+//     two groups everywhere at every Nd from 16 to 128 on the GPT-2 and 7.5B lists;
+//   * Nd < 16: one group everywhere, at the occupancy its 77 registers allow (six waves per
+//     SIMD): 3-4% faster at Nd = 8 on the GPT-2 and Llama lists than two groups at three waves
+//     per SIMD, which were in turn 3-5% faster there than the many-row kernel.
 // Columns of parameters without a gradient are skipped before any row is read.  The overflow
 // flag is ORed once per wavefront (a ballot, then one atomic), only when a value is found.
 #include "zs_reduce.h"
 
 namespace zs {
 
-// Nd from which whole tiles keep one group of rows in flight (kRowsGroup) instead of two.
-constexpr int64_t kGroupFormNd = 16;
+// Nd from which the reduce runs its many-row kernel (below).
+constexpr int64_t kBigNd = 16;
 
-template <int DT, int WHOLE>
+template <int DT, int WHOLE, int MIXED>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(DevPlan P, int64_t b_base, int64_t b_row, int64_t tile0,
                                                         int64_t n_tile, const uint16_t* __restrict__ rows,
                                                         int64_t row_stride, const uint8_t* __restrict__ live,
                                                         float* __restrict__ g32, int32_t* __restrict__ flag) {
-    reduce_body<DT, WHOLE, kRowsPipe, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
+    reduce_body<DT, WHOLE, MIXED, true>(P, b_base, b_row, tile0, n_tile, rows, row_stride, live, g32, flag, blockIdx.x, gridDim.x);
 }
 
 __global__ __launch_bounds__(kBlock) void overflow_kernel(DevPlan P, const float* __restrict__ g32,
@@ -80,12 +83,14 @@ extern "C" zero_status zero_reduce_shard(const zero_plan* plan, int64_t b, const
         L.blocks == 0)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const bool group = plan->nd >= kGroupFormNd;
-    auto kern = plan->dtype == ZERO_BF16 ? (group ? reduce_kernel<ZERO_BF16, kRowsGroup> : reduce_kernel<ZERO_BF16, kRowsPipe>)
-                                         : (group ? reduce_kernel<ZERO_FP16, kRowsGroup> : reduce_kernel<ZERO_FP16, kRowsPipe>);
-    // the one-group form runs at two blocks per CU (kTwoBlocksLds), the two-group form uncapped
-    kern<<<int(L.blocks), kBlock, group ? kTwoBlocksLds : 0u, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile,
-                                                                    L.rows, L.row_stride, L.live, L.g32, L.flag);
+    // Nd >= kBigNd: one group in flight on whole tiles, two on the others, at two blocks per CU;
+    // below, one group everywhere at the occupancy the registers allow
+    const bool big = plan->nd >= kBigNd;
+    auto kern = plan->dtype == ZERO_BF16
+                    ? (big ? reduce_kernel<ZERO_BF16, kRowsGroup, kRowsPipe> : reduce_kernel<ZERO_BF16, kRowsGroup, kRowsGroup>)
+                    : (big ? reduce_kernel<ZERO_FP16, kRowsGroup, kRowsPipe> : reduce_kernel<ZERO_FP16, kRowsGroup, kRowsGroup>);
+    kern<<<int(L.blocks), kBlock, big ? kTwoBlocksLds : 0u, s>>>(plan->dev, L.b_base, L.b_row, L.tile0, L.n_tile, L.rows,
+                                                                  L.row_stride, L.live, L.g32, L.flag);
     return check_launch("zero_reduce_shard");
 }
 

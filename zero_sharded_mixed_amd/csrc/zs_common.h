@@ -224,10 +224,11 @@ __device__ __forceinline__ bool non_finite(float f) { return (__float_as_uint(f)
 //              registers (the ZeRO-3 layer launch, which shares its registers with the pack
 //              and the unpack, and the fused reduce + Adam on whole tiles);
 //   kRowsGroup groups of kAhead rows from row 0, each group's loads then its adds, the last
-//              partial group loaded whole (the reduce's whole tiles at Nd >= 16);
+//              partial group loaded whole (the reduce: every tile below Nd = 16, the tiles inside
+//              one parameter from Nd = 16);
 //   kRowsPipe  the same groups with the next group's loads issued before the current group's
-//              adds, two groups in registers (the reduce at Nd < 16, the reduce's and the fused
-//              kernel's tiles that hold several parameters).
+//              adds, two groups in registers (the tiles that hold several parameters, in the
+//              reduce from Nd = 16 and in the fused reduce + Adam).
 // NT makes the row loads nontemporal (each wave's load covers 1 KB of whole lines).
 enum RowForm { kRowsLow, kRowsGroup, kRowsPipe };
 constexpr int kAhead = 8;
