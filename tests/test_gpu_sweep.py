@@ -47,6 +47,10 @@ def random_case(seed):
     return rng, nd, rank, numels, cap, groups, dtype
 
 
+# seeds whose plans cover Nd = 3, 13, 1031, 8, 257, 31, 100, 16, 1024, 64 and 1
+SMALL_GRID_SEEDS = [0, 1, 2, 4, 9, 10, 11, 12, 15, 16, 61]
+
+
 def finite_bits(rng, n, dtype):
     return random_bits(rng, n) & np.uint16(0xBFFF if dtype == BF16 else 0xBBFF)
 
@@ -319,3 +323,13 @@ def test_random_zero3_schedule(seed):
         o, s_ = pl.params[i, oracle.P_OFFSET], pl.params[i, oracle.P_SHARD]
         ever[o:o + s_] = True
     check_arena(pl, to_np16(st.arena), arena, to_np32(st.p32), p32, ever, dtype, "arena")
+
+
+@pytest.mark.parametrize("seed", SMALL_GRID_SEEDS)
+def test_random_plan_whole_step_small_grids(seed):
+    """The same parity with the library built with every grid capped at 37 blocks: each block
+    then takes many tiles, row groups and chunk groups in turn (the pack restages its LDS for
+    every mixed tile, the fused kernel reuses its LDS across tiles), so what is checked here is
+    the kernels' loops over their work items, which the one-shot grids never iterate."""
+    with Z._binding.library(Z._binding.SMALL_GRID_LIB_PATH):
+        test_random_plan_whole_step(seed)

@@ -328,6 +328,14 @@ def test_z3_step_ranges_match_single_buckets_and_oracle(nd, rank, dtype, check):
         assert got[0] == 0x1111 and got[-1] == 0x1111, i
 
 
+@pytest.mark.parametrize("nd,rank,dtype,check", [(8, 3, BF16, False), (64, 17, FP16, True)])
+def test_z3_step_ranges_small_grids(nd, rank, dtype, check):
+    """The ZeRO-3 launches with the library built with every grid capped at 37 blocks: the
+    reduce, pack and unpack parts then share a few blocks, each looping over many work items."""
+    with Z._binding.library(Z._binding.SMALL_GRID_LIB_PATH):
+        test_z3_step_ranges_match_single_buckets_and_oracle(nd, rank, dtype, check)
+
+
 def test_z3_step_arguments():
     """Nothing to do is allowed; counts above the maximum or ranges outside the plan are refused
     before anything runs, as are the per-bucket entry points' own errors."""

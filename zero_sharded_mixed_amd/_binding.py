@@ -7,6 +7,7 @@ CPU fallback: if the library is missing, the first call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -16,6 +17,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
+SMALL_GRID_LIB_PATH = os.path.join(_HERE, "libzero_shard_smallgrid.so")  # grids capped at a few blocks
 
 ZERO_OK, ZERO_EINVAL, ZERO_ENOMEM, ZERO_EHIP, ZERO_ERANGE = 0, -1, -2, -3, -4
 ZERO_BF16, ZERO_FP16 = 1, 2
@@ -91,12 +93,35 @@ def _scaler(plan: "Plan", t: Optional[torch.Tensor], what: str) -> Optional[int]
 def lib() -> ctypes.CDLL:
     """Load libzero_shard.so (built in place by zero_sharded_mixed_amd/build.py)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: the HIP library is not built "
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route the binding's calls to another build of the same sources while the block runs (the
+    tests run the build whose grids are capped at a few blocks through it); plans made inside
+    are destroyed by the library that made them."""
+    global _lib
+    saved = _lib
+    _lib = _load(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+_loaded = {}
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: the HIP library is not built "
                            "(python zero_sharded_mixed_amd/build.py); there is no fallback")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
     sigs = {
         "zero_plan_create": (i32, [vp, i64, i32, i32, i64, i32, ctypes.POINTER(vp)]),
@@ -127,7 +152,7 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.restype = res
         f.argtypes = args
-    _lib = L
+    _loaded[path] = L
     return L
 
 
@@ -230,6 +255,7 @@ class Plan:
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
+        self._lib = lib()  # the library that made the plan destroys it
         s = zero_plan_summary()
         _check(lib().zero_plan_get_summary(self._h, ctypes.byref(s)))
         self.n, self.nd, self.device = int(s.n_params), int(s.nd), int(s.device)
@@ -266,7 +292,7 @@ class Plan:
 
     def close(self) -> None:
         if self._h:
-            lib().zero_plan_destroy(self._h)
+            self._lib.zero_plan_destroy(self._h)
             self._h = ctypes.c_void_p(None)
 
     def __del__(self):
