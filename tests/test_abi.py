@@ -60,6 +60,24 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name)
 
 
+def test_small_grid_build_exports_the_same_symbols(L):
+    """The small-grid build the GPU tests run (the same sources, grids capped at a few blocks)
+    loads through the binding and exports every declared function; the binding's calls return
+    to the main library when its block ends."""
+    if not os.path.exists(B.SMALL_GRID_LIB_PATH):
+        from zero_sharded_mixed_amd import build
+        build.build()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.SMALL_GRID_LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(zero_\w+)$", out, flags=re.M))
+    with B.library(B.SMALL_GRID_LIB_PATH) as S:
+        assert B.lib() is S and S is not L
+        for name in declared_functions():
+            assert name in exported, name
+            assert hasattr(S, name)
+    assert B.lib() is L
+
+
 def _create(L, numels, nd=8, rank=0, bucket_bytes=0, dtype=1, out=True):
     arr = (ctypes.c_int64 * max(len(numels), 1))(*numels)
     h = ctypes.c_void_p(123)
