@@ -21,10 +21,16 @@ _SETUPS = {}
 
 def setup_workload(cfg):
     """MlpModel (one bucket) or the GPT-2 1.5B-shaped list (four 500M-element buckets), full
-    emulation: every virtual rank's gradients packed into its own rows beforehand."""
+    emulation: every virtual rank's gradients packed into its own rows beforehand.  "1-nd64" is
+    the MlpModel at 64 virtual ranks, rank 17: the reduce's many-row kernel, launched with its
+    LDS reservation, inside the graph."""
     if cfg in _SETUPS:
         return _SETUPS[cfg]
-    w = W.workload(cfg)
+    if cfg == "1-nd64":
+        w = W.workload(1)
+        w.nd, w.rank = 64, 17
+    else:
+        w = W.workload(cfg)
     say(f"graph setup: {w.name}, Nd={w.nd}, rank {w.rank}")
     st = Z.ShardStep(w.numels, w.nd, w.rank, w.bucket_bytes, w.dtype)
     masters = W.masters(w, DEV)
@@ -56,7 +62,7 @@ def snapshot(st, lp):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, "1-nd64", 2])
 @pytest.mark.parametrize("path", ["unfused", "fused"])
 def test_captured_step_replays_like_eager_steps(cfg, path):
     w, st, lp, lp_ptrs, own_ptrs, rows = setup_workload(cfg)
